@@ -1,0 +1,266 @@
+"""libcpattn Python binding: the single-GPU hot path of decode / prefill context
+parallelism on MI355X, as thin argument marshalling over the C ABI
+(include/cpattn.h).
+
+Every function takes torch tensors that live on the GPU (torch supplies the
+device memory and the current HIP stream; all computation runs in the HIP
+kernels of libcpattn.so).  Errors raise ``CpError`` carrying the library's
+status and message.  There is no fallback: if libcpattn.so is missing the
+first call raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (CP_BF16, CP_E_HIP, CP_E_INVALID, CP_E_UNSUPPORTED, CP_E_WORKSPACE, CP_F32,
+                   CP_FP8_E4M3FN, CP_KV_DENSE, CP_KV_PAGED, CP_OK, CP_OP_DECODE_GQA,
+                   CP_OP_DECODE_MLA, CP_OP_PREFILL, CP_SLOT_INVALID, CP_SLOT_NOT_MINE)
+
+__all__ = [
+    "CpError", "cp_local_seq_lens", "cp_slot_map", "cp_cache_write", "cp_decode_attn_partial_gqa",
+    "cp_decode_attn_partial_mla", "cp_lse_merge", "pcp_prefill_attn_causal", "cp_workspace_bytes",
+    "gqa_args", "mla_args", "prefill_args", "library_path",
+]
+
+_DT = {torch.float32: CP_F32, torch.bfloat16: CP_BF16, torch.float8_e4m3fn: CP_FP8_E4M3FN}
+
+
+class CpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = _lib.load()
+        self.status = status
+        msg = lib.cp_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {lib.cp_status_str(status).decode()}: {msg}")
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _check(st: int, where: str):
+    if st != CP_OK:
+        raise CpError(st, where)
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libcpattn takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libcpattn takes contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dt(t) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {t.dtype}") from None
+
+
+def _i32(t, name):
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32")
+    return _ptr(t)
+
+
+# ---------------------------------------------------------------------------
+# ownership and paging
+# ---------------------------------------------------------------------------
+
+def cp_local_seq_lens(seq_lens, rank: int, N: int, I: int, out=None, stream=None):
+    """Local KV length of each request on ``rank`` (int32 [B])."""
+    lib = _lib.load()
+    B = seq_lens.numel()
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=seq_lens.device)
+    _check(lib.cp_local_seq_lens(B, _i32(seq_lens, "seq_lens"), rank, N, I, _i32(out, "out"),
+                                 _stream(stream)), "cp_local_seq_lens")
+    return out
+
+
+def cp_slot_map(req, pos, block_table, rank: int, N: int, I: int, bs: int, max_blocks=None,
+                out=None, stream=None):
+    """Slot of every token on ``rank`` (int64 [T]; -1 not mine, -2 invalid)."""
+    lib = _lib.load()
+    T = req.numel()
+    B, stride = block_table.shape
+    if out is None:
+        out = torch.empty(T, dtype=torch.int64, device=req.device)
+    mb = stride if max_blocks is None else max_blocks
+    _check(lib.cp_slot_map(T, _i32(req, "req"), _i32(pos, "pos"),
+                           _i32(block_table, "block_table"), B, stride, mb, rank, N, I, bs,
+                           _ptr(out), _stream(stream)), "cp_slot_map")
+    return out
+
+
+def cp_cache_write(slot, k, v, k_cache, v_cache, bs: int, stream=None):
+    """Scatter token rows to their slots.  GQA: k, v [T][Hkv][D] into caches
+    [num_blocks][Hkv][bs][D].  MLA: k [T][Dk] latent rows, v = v_cache = None,
+    cache [num_blocks][bs][Dk]."""
+    lib = _lib.load()
+    T = slot.numel()
+    if slot.dtype != torch.int64:
+        raise ValueError("slot must be int64")
+    if v is None:
+        heads, row = 1, k.shape[-1]
+    else:
+        heads, row = k.shape[1], k.shape[2]
+    num_blocks = k_cache.shape[0]
+    if k.dtype != k_cache.dtype or (v is not None and v.dtype != v_cache.dtype):
+        raise ValueError("rows and cache must share a dtype")
+    _check(lib.cp_cache_write(T, _ptr(slot), _ptr(k), _ptr(v), heads, row, _dt(k), _ptr(k_cache),
+                              _ptr(v_cache), num_blocks, bs, _stream(stream)), "cp_cache_write")
+
+
+# ---------------------------------------------------------------------------
+# decode partials
+# ---------------------------------------------------------------------------
+
+def gqa_args(q, k_cache, v_cache, block_table, local_len, scale, out, lse):
+    B, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shape mismatch")
+    return _lib.CpGqaArgs(q=_ptr(q), k_cache=_ptr(k_cache), v_cache=_ptr(v_cache),
+                          block_table=_i32(block_table, "block_table"),
+                          local_len=_i32(local_len, "local_len"), B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs,
+                          bt_stride=block_table.shape[1], num_blocks=nb, scale=scale, dt=_dt(q),
+                          out=_ptr(out), lse=_ptr(lse))
+
+
+def mla_args(q, kv_cache, block_table, local_len, scale, out, lse, Dv=512, kv_scale=1.0):
+    B, H, Dk = q.shape
+    nb, bs, Dk2 = kv_cache.shape
+    if Dk2 != Dk:
+        raise ValueError("latent width mismatch")
+    return _lib.CpMlaArgs(q=_ptr(q), kv_cache=_ptr(kv_cache),
+                          block_table=_i32(block_table, "block_table"),
+                          local_len=_i32(local_len, "local_len"), B=B, H=H, Dk=Dk, Dv=Dv, bs=bs,
+                          bt_stride=block_table.shape[1], num_blocks=nb, scale=scale,
+                          kv_dt=_dt(kv_cache), kv_scale=kv_scale, out=_ptr(out), lse=_ptr(lse))
+
+
+def cp_workspace_bytes(op: int, args) -> int:
+    n = _lib.load().cp_workspace_bytes(op, ctypes.byref(args))
+    if n == ctypes.c_size_t(-1).value:
+        raise CpError(CP_E_INVALID, "cp_workspace_bytes")
+    return int(n)
+
+
+def _workspace(op, args, device, workspace):
+    need = cp_workspace_bytes(op, args)
+    if need == 0:
+        return None, 0
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def cp_decode_attn_partial_gqa(q, k_cache, v_cache, block_table, local_len, scale, out=None,
+                               lse=None, workspace=None, stream=None):
+    """Partial attention of q [B][Hq][D] over one shard's paged KV; returns
+    (out fp32 [B][Hq][D], lse fp32 [B][Hq])."""
+    lib = _lib.load()
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty(B, Hq, D, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, Hq, dtype=torch.float32, device=q.device)
+    a = gqa_args(q, k_cache, v_cache, block_table, local_len, scale, out, lse)
+    ws, nws = _workspace(CP_OP_DECODE_GQA, a, q.device, workspace)
+    _check(lib.cp_decode_attn_partial_gqa(ctypes.byref(a), _ptr(ws), nws, _stream(stream)),
+           "cp_decode_attn_partial_gqa")
+    return out, lse
+
+
+def cp_decode_attn_partial_mla(q, kv_cache, block_table, local_len, scale, Dv=512, kv_scale=1.0,
+                               out=None, lse=None, workspace=None, stream=None):
+    """Absorbed-MLA partial attention of q [B][H][Dk] (bf16) over one shard's
+    latent cache [num_blocks][bs][Dk]; returns (out fp32 [B][H][Dv], lse [B][H])."""
+    lib = _lib.load()
+    B, H, _ = q.shape
+    if out is None:
+        out = torch.empty(B, H, Dv, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, H, dtype=torch.float32, device=q.device)
+    a = mla_args(q, kv_cache, block_table, local_len, scale, out, lse, Dv=Dv, kv_scale=kv_scale)
+    ws, nws = _workspace(CP_OP_DECODE_MLA, a, q.device, workspace)
+    _check(lib.cp_decode_attn_partial_mla(ctypes.byref(a), _ptr(ws), nws, _stream(stream)),
+           "cp_decode_attn_partial_mla")
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# merge
+# ---------------------------------------------------------------------------
+
+def cp_lse_merge(part_out, part_lse, out=None, lse_out=None, out_dtype=torch.float32,
+                 stream=None):
+    """Exact merge of part_out [n][rows...][Dv] with part_lse [n][rows...]."""
+    lib = _lib.load()
+    n = part_out.shape[0]
+    Dv = part_out.shape[-1]
+    rows = part_lse[0].numel()
+    if part_out.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise ValueError("partials must be fp32")
+    if part_out.numel() != n * rows * Dv:
+        raise ValueError("part_out / part_lse shape mismatch")
+    if out is None:
+        out = torch.empty(part_out.shape[1:], dtype=out_dtype, device=part_out.device)
+    if lse_out is None:
+        lse_out = torch.empty(part_lse.shape[1:], dtype=torch.float32, device=part_out.device)
+    _check(lib.cp_lse_merge(n, rows, Dv, _ptr(part_out), _ptr(part_lse), _ptr(out), _dt(out),
+                            _ptr(lse_out), _stream(stream)), "cp_lse_merge")
+    return out, lse_out
+
+
+# ---------------------------------------------------------------------------
+# PCP causal prefill
+# ---------------------------------------------------------------------------
+
+def prefill_args(q, P, pcp_rank, pcp_size, scale, out, lse, *, k=None, v=None, k_cache=None,
+                 v_cache=None, block_table=None, local_len=0):
+    C, Hq, D = q.shape
+    if k is not None:
+        src, Hkv = CP_KV_DENSE, k.shape[1]
+        nb, bs, stride = 0, 16, 1
+    else:
+        src, Hkv = CP_KV_PAGED, k_cache.shape[1]
+        nb, bs, stride = k_cache.shape[0], k_cache.shape[2], block_table.numel()
+    return _lib.CpPrefillArgs(
+        q=_ptr(q), C=C, P=P, pcp_rank=pcp_rank, pcp_size=pcp_size, Hq=Hq, Hkv=Hkv, D=D,
+        scale=scale, kv_source=src, k=_ptr(k), v=_ptr(v), k_cache=_ptr(k_cache),
+        v_cache=_ptr(v_cache), block_table=None if block_table is None else _i32(block_table, "bt"),
+        local_len=int(local_len), bs=bs, bt_stride=stride, num_blocks=nb, out=_ptr(out),
+        lse=_ptr(lse))
+
+
+def pcp_prefill_attn_causal(q, P, pcp_rank, pcp_size, scale, *, k=None, v=None, k_cache=None,
+                            v_cache=None, block_table=None, local_len=0, out=None, lse=None,
+                            stream=None):
+    """Rank ``pcp_rank``'s two pieces of the chunk q [C][Hq][D] (bf16) against
+    either the chunk's own keys (k, v: causal) or one DCP shard of the prefix
+    (k_cache, v_cache, block_table, local_len).  Returns (out fp32
+    [2][C/2N][Hq][D], lse fp32 [2][C/2N][Hq])."""
+    lib = _lib.load()
+    C, Hq, D = q.shape
+    c = C // (2 * pcp_size)
+    if out is None:
+        out = torch.empty(2, c, Hq, D, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(2, c, Hq, dtype=torch.float32, device=q.device)
+    a = prefill_args(q, P, pcp_rank, pcp_size, scale, out, lse, k=k, v=v, k_cache=k_cache,
+                     v_cache=v_cache, block_table=block_table, local_len=local_len)
+    _check(lib.pcp_prefill_attn_causal(ctypes.byref(a), None, 0, _stream(stream)),
+           "pcp_prefill_attn_causal")
+    return out, lse

@@ -1,0 +1,107 @@
+// internal.hpp -- shared host/device helpers of libcpattn (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "cpattn.h"
+
+namespace cpattn {
+
+// ---------------------------------------------------------------- host side
+
+// Records a message for cp_last_error() (per host thread) and returns `st`.
+cp_status fail(cp_status st, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+// Returns CP_E_HIP with a message if the last launch on this thread failed.
+cp_status check_launch(const char *what);
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int elem_bytes(cp_dtype dt) {
+    switch (dt) {
+    case CP_F32: return 4;
+    case CP_BF16: return 2;
+    case CP_FP8_E4M3FN: return 1;
+    }
+    return 0;
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Split-K plans: how a decode call divides each request's local tokens.
+struct GqaPlan {
+    int32_t split_tokens;  // tokens per work item (multiple of 64)
+    int32_t nsplit;        // work items per (request, kv head)
+    size_t ws_bytes;       // partial outputs + LSEs, 0 when nsplit == 1
+};
+GqaPlan plan_gqa(const cp_gqa_args &a);
+
+struct MlaPlan {
+    int32_t split_tokens;
+    int32_t nsplit;
+    size_t ws_bytes;
+};
+MlaPlan plan_mla(const cp_mla_args &a);
+
+// Exact LSE merge over strided partials (shared by cp_lse_merge and the
+// split-K combine of the decode kernels).  Part i of row r:
+//   out: part_out[i*o_part_stride + r*o_row_stride + d],
+//   lse: part_lse[i*l_part_stride + r*l_row_stride].
+// Output row r at out[r*Dv], lse_out[r] (lse_out may be null).
+struct MergeDesc {
+    int32_t n_parts;
+    int64_t rows;
+    int32_t Dv;
+    const float *part_out;
+    const float *part_lse;
+    int64_t o_part_stride, o_row_stride;
+    int64_t l_part_stride, l_row_stride;
+    void *out;
+    cp_dtype out_dt;
+    float *lse_out;
+};
+cp_status launch_merge(const MergeDesc &m, hipStream_t stream);
+
+// ---------------------------------------------------------------- device side
+
+// Global-memory byte pointer: keeps loads on the global (not flat) path.
+#define CP_GLOBAL __attribute__((address_space(1)))
+typedef const uint8_t CP_GLOBAL gbyte;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+inline gbyte *to_global(const void *p) { return (gbyte *)(p); }
+
+__device__ __forceinline__ u32x4 load16(gbyte *p) {
+    return *reinterpret_cast<const CP_GLOBAL u32x4 *>(p);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace cpattn

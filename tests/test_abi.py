@@ -1,0 +1,115 @@
+"""CPU checks of the C ABI: the built library loads, exports every function
+include/cpattn.h declares, its argument structs have the layout the Python
+binding assumes (checked against gcc's own offsetof), and host-side argument
+validation rejects bad calls before any launch (no GPU needed for those)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from kv_context_parallelism_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpattn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_six_calls():
+    names = _declared_functions()
+    for n in ["cp_slot_map", "cp_cache_write", "cp_decode_attn_partial_gqa",
+              "cp_decode_attn_partial_mla", "cp_lse_merge", "pcp_prefill_attn_causal"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib.load()
+    declared = _declared_functions()
+    assert set(declared) == set(_lib.SIGNATURES), "binding and header disagree"
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert set(declared) <= exported
+
+
+def test_status_strings_and_version():
+    lib = _lib.load()
+    assert lib.cp_abi_version() == 1
+    assert lib.cp_status_str(0) == b"CP_OK"
+    assert lib.cp_status_str(3) == b"CP_E_WORKSPACE"
+
+
+_LAYOUT_C = r"""
+#include <stddef.h>
+#include <stdio.h>
+#include "cpattn.h"
+#define F(T, f) printf(#T " " #f " %zu\n", offsetof(T, f));
+int main(void) {
+  printf("cp_gqa_args sizeof %zu\n", sizeof(cp_gqa_args));
+  printf("cp_mla_args sizeof %zu\n", sizeof(cp_mla_args));
+  printf("cp_prefill_args sizeof %zu\n", sizeof(cp_prefill_args));
+  %FIELDS%
+  return 0;
+}
+"""
+
+
+@pytest.mark.parametrize("cname,pytype", [("cp_gqa_args", _lib.CpGqaArgs),
+                                          ("cp_mla_args", _lib.CpMlaArgs),
+                                          ("cp_prefill_args", _lib.CpPrefillArgs)])
+def test_struct_layout_matches_c(tmp_path, cname, pytype):
+    fields = "\n".join(f"F({cname}, {f})" for f, _ in pytype._fields_)
+    src = tmp_path / "layout.c"
+    src.write_text(_LAYOUT_C.replace("%FIELDS%", fields))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.dirname(HEADER),
+                    "-I", "/opt/rocm/include", str(src), "-o", str(exe)], check=True)
+    lines = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    got = {}
+    for ln in lines.splitlines():
+        t, f, v = ln.split()
+        got[(t, f)] = int(v)
+    assert got[(cname, "sizeof")] == ctypes.sizeof(pytype)
+    for f, _ in pytype._fields_:
+        assert got[(cname, f)] == getattr(pytype, f).offset, f
+
+
+def test_host_validation_rejects_bad_arguments():
+    lib = _lib.load()
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    # rank outside [0, N)
+    assert lib.cp_slot_map(4, fake, fake, fake, 1, 4, 4, 4, 4, 4, 16, fake, None) == 1
+    # interleave 0
+    assert lib.cp_local_seq_lens(4, fake, 0, 4, 0, fake, None) == 1
+    # merge: Dv not a multiple of 4 -> unsupported; zero parts -> invalid
+    assert lib.cp_lse_merge(2, 10, 6, fake, fake, fake, 0, fake, None) == 2
+    assert lib.cp_lse_merge(0, 10, 8, fake, fake, fake, 0, fake, None) == 1
+    # cache write with v but no v_cache
+    assert lib.cp_cache_write(4, fake, fake, fake, 1, 64, 1, fake, None, 8, 16, None) == 1
+    # GQA: Hq not a multiple of Hkv; unsupported head dim; workspace missing
+    a = _lib.CpGqaArgs(q=16, k_cache=16, v_cache=16, block_table=16, local_len=16, B=2, Hq=6,
+                       Hkv=4, D=128, bs=16, bt_stride=8, num_blocks=64, scale=0.1, dt=1, out=16,
+                       lse=16)
+    assert lib.cp_decode_attn_partial_gqa(ctypes.byref(a), None, 0, None) == 1
+    a.Hq, a.D = 8, 96
+    assert lib.cp_decode_attn_partial_gqa(ctypes.byref(a), None, 0, None) == 2
+    a.D, a.bs = 128, 24
+    assert lib.cp_decode_attn_partial_gqa(ctypes.byref(a), None, 0, None) == 2
+    a.bs, a.bt_stride = 16, 4096
+    need = lib.cp_workspace_bytes(1, ctypes.byref(a))
+    assert need > 0
+    assert lib.cp_decode_attn_partial_gqa(ctypes.byref(a), None, 0, None) == 3
+    assert b"workspace" in lib.cp_last_error()
+    # prefill: chunk not aligned to 2N
+    p = _lib.CpPrefillArgs(q=16, C=100, P=0, pcp_rank=0, pcp_size=8, Hq=32, Hkv=8, D=128,
+                           scale=0.1, kv_source=0, k=16, v=16, out=16, lse=16)
+    assert lib.pcp_prefill_attn_causal(ctypes.byref(p), None, 0, None) in (1, 2)
