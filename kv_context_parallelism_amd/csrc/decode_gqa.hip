@@ -36,6 +36,7 @@ namespace cpattn {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kMaxSplitBlocks = 64;  // block ids staged per work item (split <= 64 blocks)
 
 struct GqaParams {
     const gbyte *q, *kc, *vc;
@@ -89,13 +90,14 @@ struct GqaTraits {
     static_assert(16 % RG == 0, "one PV load instruction must stay inside a 16-token group");
 };
 
-template <int EB, int D, int G, int TILE>
-__global__ void __launch_bounds__(64 * kWaves) gqa_decode_kernel(GqaParams p) {
+template <int EB, int D, int G, int TILE, int MIN_WG_PER_CU>
+__global__ void __launch_bounds__(64 * kWaves, MIN_WG_PER_CU) gqa_decode_kernel(GqaParams p) {
     using Tr = GqaTraits<EB, D, G, TILE>;
     constexpr int ROWB = Tr::ROWB, CH = Tr::CH, EPC = Tr::EPC, NCQ = Tr::NCQ, RG = Tr::RG;
     constexpr int NPASS = Tr::NPASS, TPL = Tr::TPL;
     constexpr bool kBf16 = (EB == 2);
     __shared__ uint32_t s_p[kWaves][Tr::PWORDS];
+    __shared__ int32_t s_bt[kWaves][kMaxSplitBlocks];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -154,46 +156,69 @@ __global__ void __launch_bounds__(64 * kWaves) gqa_decode_kernel(GqaParams p) {
     }
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
-    for (int32_t tb = s0; tb < s1; tb += TILE) {
-        // physical block of each 16-token group of the tile (uniform loads)
-        constexpr int NG = TILE / 16;
-        int64_t grp_row[NG];  // first cache row of the group's tokens for head g
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi) {
-            const int32_t lb = tb + gi * 16;
-            int64_t row = 0;
-            if (lb < s1) {
-                int32_t phys = bt_row[lb >> p.bs_log2];
-                const bool ok = phys >= 0 && (int64_t)phys < p.num_blocks;
-                bad |= !ok;
-                phys = ok ? phys : 0;
-                row = ((int64_t)phys * p.Hkv + g) * bs + (lb & (bs - 1));
-            }
-            grp_row[gi] = row;
-        }
+    // ---- this split's physical block ids, staged once in LDS ----
+    const int32_t blk0 = s0 >> p.bs_log2;
+    const int32_t nblk = ((s1 - 1) >> p.bs_log2) - blk0 + 1;
+    for (int i = lane; i < nblk; i += 64) {
+        int32_t phys = bt_row[blk0 + i];
+        const bool ok = phys >= 0 && (int64_t)phys < p.num_blocks;
+        bad |= !ok;
+        s_bt[wave][i] = ok ? phys : 0;
+    }
+    bad = __ballot(bad) != 0;
+    wave_sync();
 
-        // ---- loads: K in the QK layout, V in the PV layout ----
-        u32x4 kreg[NPASS][NCQ];
-        bool kval[NPASS];
+    // First cache row (head g) of the 16-token group starting at local index lb.
+    // Groups past the split's end map to the split's first group, so every
+    // address formed below stays inside the cache.
+    auto group_row = [&](int32_t lb) -> int64_t {
+        const int32_t gsel = lb < s1 ? lb : s0;
+        const int32_t phys =
+            __builtin_amdgcn_readfirstlane(s_bt[wave][(gsel >> p.bs_log2) - blk0]);
+        return ((int64_t)phys * p.Hkv + g) * bs + (gsel & (bs - 1));
+    };
+    // K of tile tb in the QK layout.  Rows of tokens past the split's end lie in
+    // an allocated block of this split; their scores are replaced by -inf.
+    auto load_k = [&](int32_t tb, u32x4 (&kreg)[NPASS][NCQ]) {
 #pragma unroll
         for (int pp = 0; pp < NPASS; ++pp) {
-            kval[pp] = (tb + pp * 16 + tp) < s1;
-            const gbyte *rowp = p.kc + (grp_row[pp] + tp) * ROWB;
+            const gbyte *rowp = p.kc + (group_row(tb + pp * 16) + tp) * ROWB;
 #pragma unroll
-            for (int j = 0; j < NCQ; ++j) {
-                kreg[pp][j] = zero4;
-                if (kval[pp]) kreg[pp][j] = load16(rowp + (j * 4 + qd) * 16);
-            }
+            for (int j = 0; j < NCQ; ++j) kreg[pp][j] = load16(rowp + (j * 4 + qd) * 16);
         }
-        u32x4 vreg[TPL];
+    };
+    // V of tile tb in the PV layout; zero_tail() clears rows past the split's
+    // end (their probability is 0, but the row may hold NaN poison).
+    auto load_v = [&](int32_t tb, u32x4 (&vreg)[TPL]) {
+        constexpr int NG = TILE / 16;
+        int64_t grow[NG];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) grow[gi] = group_row(tb + gi * 16);
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
-            const int t = i * RG + R;  // token within the tile
-            const bool ok = (tb + t) < s1;
-            const gbyte *rowp = p.vc + (grp_row[(i * RG) / 16] + ((i * RG) & 15) + R) * ROWB;
-            vreg[i] = zero4;
-            if (ok) vreg[i] = load16(rowp + c * 16);
+            const gbyte *rowp = p.vc + (grow[(i * RG) / 16] + ((i * RG) & 15) + R) * ROWB;
+            vreg[i] = load16(rowp + c * 16);
         }
+    };
+    auto zero_tail = [&](int32_t tb, u32x4 (&vreg)[TPL]) {
+#pragma unroll
+        for (int i = 0; i < TPL; ++i)
+            if (tb + i * RG + R >= s1) vreg[i] = zero4;
+    };
+
+    // Staggered pipeline: K of the next tile is requested right after this
+    // tile's scores are formed (overlapping softmax and PV), V of the next tile
+    // right after this tile's PV (overlapping the next scores).
+    u32x4 kreg[NPASS][NCQ];
+    u32x4 vreg[TPL];
+    load_k(s0, kreg);
+    load_v(s0, vreg);
+    for (int32_t tb = s0; tb < s1; tb += TILE) {
+        const int32_t tn = tb + TILE;
+        if (tn > s1) zero_tail(tb, vreg);  // only the split's last tile can be partial
+        bool kval[NPASS];
+#pragma unroll
+        for (int pp = 0; pp < NPASS; ++pp) kval[pp] = (tb + pp * 16 + tp) < s1;
 
         // ---- scores (log2 domain) ----
         float s[NPASS][G];
@@ -215,6 +240,8 @@ __global__ void __launch_bounds__(64 * kWaves) gqa_decode_kernel(GqaParams p) {
                 if constexpr (kBf16) a *= p.qk_scale;
                 s[pp][hh] = kval[pp] ? a : -INFINITY;
             }
+
+        if (tn < s1) load_k(tn, kreg);
 
         // ---- online softmax: wave-wide running max per head ----
 #pragma unroll
@@ -297,6 +324,7 @@ __global__ void __launch_bounds__(64 * kWaves) gqa_decode_kernel(GqaParams p) {
                 }
             }
         }
+        if (tn < s1) load_v(tn, vreg);
     }
 
     // ---- finish: sum the per-lane pieces, normalise, write o_i and L_i ----
@@ -343,7 +371,12 @@ cp_status launch_gqa(const GqaParams &p, int64_t items, hipStream_t stream) {
     } else {
         const int64_t blocks = ceil_div(items, kWaves);
         if (blocks > 0x7fffffff) return fail(CP_E_UNSUPPORTED, "gqa decode: too many work items");
-        hipLaunchKernelGGL((gqa_decode_kernel<EB, D, G, kTile>), dim3((unsigned)blocks),
+        // Two workgroups (8 waves) per CU when the tile's registers fit in 256
+        // VGPRs, else one (wider groups / fp32 rows) to avoid spills.
+        using Tr = GqaTraits<EB, D, G, kTile>;
+        constexpr int kEst = QREGS + Tr::NPASS * Tr::NCQ * 4 + Tr::TPL * 4 + G * Tr::EPC + 40;
+        constexpr int kMinWg = kEst <= 200 ? 2 : 1;
+        hipLaunchKernelGGL((gqa_decode_kernel<EB, D, G, kTile, kMinWg>), dim3((unsigned)blocks),
                            dim3(64 * kWaves), 0, stream, p);
         return check_launch("cp_decode_attn_partial_gqa");
     }
@@ -371,11 +404,26 @@ int log2_exact(int32_t x) {
 
 GqaPlan plan_gqa(const cp_gqa_args &a) {
     GqaPlan pl{};
+    if (gqa_rows_supported(a)) {
+        // row-layout kernel: one partial slot per launched wave plus one per
+        // (request, KV head) boundary, then a (first, count) table
+        const int G = a.Hq / a.Hkv;
+        pl.rows = true;
+        pl.waves = gqa_rows_waves();
+        const size_t slots = (size_t)pl.waves + (size_t)a.B * a.Hkv;
+        pl.ws_bytes = slots * G * (a.D + 1) * sizeof(float) + (size_t)a.B * a.Hkv * 2 * 4 + 512;
+        return pl;
+    }
+    // General kernel: split the capacity of each (request, KV head) into work
+    // items of S tokens so that about 8K items exist; the hardware dispatcher
+    // then balances the tail at the granularity of one item.  S is a power of
+    // two in [64, 512] and at most 64 blocks (the LDS staging of block ids).
     const int64_t cap = (int64_t)a.bt_stride * a.bs;
     const int64_t heads = (int64_t)a.B * (a.Hkv > 0 ? a.Hkv : 1);
-    int32_t S = 256;
-    while (S > 64 && heads * ceil_div(cap, S) < 2048) S /= 2;
-    pl.split_tokens = S;
+    int64_t S = 512;
+    while (S > 64 && heads * ceil_div(cap, S) < 8192) S /= 2;
+    while (S > 64 && S / (a.bs > 0 ? a.bs : 1) > kMaxSplitBlocks) S /= 2;
+    pl.split_tokens = (int32_t)S;
     pl.nsplit = (int32_t)(cap > 0 ? ceil_div(cap, S) : 1);
     pl.ws_bytes = pl.nsplit > 1 ? (size_t)a.B * a.Hq * pl.nsplit * (a.D + 1) * sizeof(float) + 256
                                 : 0;
@@ -415,6 +463,33 @@ extern "C" cp_status cp_decode_attn_partial_gqa(const cp_gqa_args *a, void *ws, 
     if (pl.ws_bytes > 0 && (!ws || ws_bytes < pl.ws_bytes))
         return fail(CP_E_WORKSPACE, "gqa decode: workspace of %zu bytes needed, %zu given",
                     pl.ws_bytes, ws_bytes);
+
+    if (pl.rows) {
+        const int G = a->Hq / a->Hkv;
+        const size_t slots = (size_t)pl.waves + (size_t)a->B * a->Hkv;
+        float *ws_o = static_cast<float *>(ws);
+        float *ws_l = ws_o + slots * G * a->D;
+        int32_t *seg = reinterpret_cast<int32_t *>(
+            (reinterpret_cast<uintptr_t>(ws_l + slots * G) + 255) & ~uintptr_t(255));
+        cp_status st = gqa_rows_launch(*a, bs_log2, ws_o, ws_l, seg, pl.waves, stream);
+        if (st != CP_OK) return st;
+        MergeDesc m;
+        m.seg = seg;
+        m.rows_per_seg = G;
+        m.n_parts = 0;
+        m.rows = (int64_t)a->B * a->Hq;
+        m.Dv = a->D;
+        m.part_out = ws_o;
+        m.part_lse = ws_l;
+        m.o_part_stride = (int64_t)G * a->D;
+        m.o_row_stride = a->D;
+        m.l_part_stride = G;
+        m.l_row_stride = 1;
+        m.out = a->out;
+        m.out_dt = CP_F32;
+        m.lse_out = a->lse;
+        return launch_merge(m, stream);
+    }
 
     GqaParams p;
     p.q = to_global(a->q);

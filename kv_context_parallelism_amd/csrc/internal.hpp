@@ -32,9 +32,11 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Split-K plans: how a decode call divides each request's local tokens.
 struct GqaPlan {
-    int32_t split_tokens;  // tokens per work item (multiple of 64)
-    int32_t nsplit;        // work items per (request, kv head)
-    size_t ws_bytes;       // partial outputs + LSEs, 0 when nsplit == 1
+    bool rows;             // balanced row-layout kernel (256-byte rows) or the general one
+    int32_t split_tokens;  // general kernel: tokens per work item (multiple of 64)
+    int32_t nsplit;        // general kernel: work items per (request, kv head)
+    int32_t waves;         // row kernel: waves launched (one per resident slot)
+    size_t ws_bytes;       // partial outputs + LSEs (+ segment table), 0 if none
 };
 GqaPlan plan_gqa(const cp_gqa_args &a);
 
@@ -51,6 +53,14 @@ MlaPlan plan_mla(const cp_mla_args &a);
 //   lse: part_lse[i*l_part_stride + r*l_row_stride].
 // Output row r at out[r*Dv], lse_out[r] (lse_out may be null).
 struct MergeDesc {
+    // Optional per-row-group segment table: when seg != nullptr, row r belongs
+    // to group r / rows_per_seg with (first slot, part count) at seg[2*group];
+    // part i of row r then sits at slot first+i and the strides below apply to
+    // slots: out at part_out[(first+i)*o_part_stride + (r % rows_per_seg)*o_row_stride],
+    // LSE at part_lse[(first+i)*l_part_stride + (r % rows_per_seg)*l_row_stride].
+    // A count of 0 gives an all-zero row with LSE -inf.
+    const int32_t *seg = nullptr;
+    int32_t rows_per_seg = 1;
     int32_t n_parts;
     int64_t rows;
     int32_t Dv;
@@ -63,6 +73,15 @@ struct MergeDesc {
     float *lse_out;
 };
 cp_status launch_merge(const MergeDesc &m, hipStream_t stream);
+
+// Compute units of the current device (cached per device).
+int device_cus();
+
+// Row-layout GQA decode kernel (256-byte KV rows), decode_gqa_rows.hip.
+bool gqa_rows_supported(const cp_gqa_args &a);
+int gqa_rows_waves();
+cp_status gqa_rows_launch(const cp_gqa_args &a, int bs_log2, float *ws_o, float *ws_l,
+                          int32_t *seg, int32_t W, hipStream_t stream);
 
 // ---------------------------------------------------------------- device side
 

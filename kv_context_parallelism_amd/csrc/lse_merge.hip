@@ -7,82 +7,158 @@
 // Bottleneck ...", section 3: correct_attn after the output exchange.)
 //
 // HBM-bound: every partial element is read once, every output written once.
-// A row is handled by Dv/4 threads, each owning one float4 column slice, so
-// loads of one part are fully coalesced; the n LSEs of a row are re-read by
-// each of its threads from cache.
+// One 256-thread workgroup per output row: the row's LSEs are reduced
+// (max, then sum of weights) across the block, then thread (column c, group
+// gi) accumulates float4 column c over the parts gi, gi+G, ..., and the G
+// group sums are added in LDS.  Rows are independent, so the grid is one
+// block per row and the loads of many rows are in flight at once.
 #include <math.h>
 
 #include "internal.hpp"
 
 namespace cpattn {
 
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kCachedWeights = 2048;  // weights kept in LDS; beyond that, recomputed
+
+__device__ __forceinline__ float block_reduce(float v, bool is_max, float *s_red) {
+    for (int x = 32; x >= 1; x >>= 1) {
+        const float o = __shfl_xor(v, x, 64);
+        v = is_max ? fmaxf(v, o) : v + o;
+    }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __syncthreads();
+    if (lane == 0) s_red[wave] = v;
+    __syncthreads();
+    v = s_red[0];
+    for (int i = 1; i < kThreads / 64; ++i) v = is_max ? fmaxf(v, s_red[i]) : v + s_red[i];
+    return v;
+}
+
 template <bool kBf16Out>
-__global__ void __launch_bounds__(256) merge_kernel(MergeDesc m, int32_t tpr, int32_t rpb) {
-    const int32_t sub = threadIdx.x / tpr;
-    const int32_t lane = threadIdx.x - sub * tpr;
-    const int64_t row = (int64_t)blockIdx.x * rpb + sub;
-    if (sub >= rpb || row >= m.rows) return;
+__global__ void __launch_bounds__(kThreads) merge_rows_kernel(MergeDesc m) {
+    __shared__ float s_w[kCachedWeights];
+    __shared__ float s_red[kThreads / 64];
+    __shared__ float4 s_acc[kThreads];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
     const float *lp = m.part_lse + row * m.l_row_stride;
+    const float *obase = m.part_out + row * m.o_row_stride;
+    if (m.seg) {  // parts of this row live at slots first .. first+count-1
+        const int64_t grp = row / m.rows_per_seg, sub = row % m.rows_per_seg;
+        const int64_t first = m.seg[2 * grp];
+        m.n_parts = m.seg[2 * grp + 1];
+        lp = m.part_lse + first * m.l_part_stride + sub * m.l_row_stride;
+        obase = m.part_out + first * m.o_part_stride + sub * m.o_row_stride;
+    }
+
+    // 1. l = max_i L_i (NaN anywhere poisons the row)
     float lmax = -INFINITY;
-    bool any_nan = false;
-    for (int32_t i = 0; i < m.n_parts; ++i) {
-        float L = lp[i * m.l_part_stride];
-        any_nan |= (L != L);
+    int nan = 0;
+    for (int i = tid; i < m.n_parts; i += kThreads) {
+        const float L = lp[(int64_t)i * m.l_part_stride];
+        nan |= (L != L);
         lmax = fmaxf(lmax, L);
     }
+    lmax = block_reduce(lmax, true, s_red);
+    nan = __syncthreads_or(nan);
+    // 2. a_i = exp(L_i - l), their sum
     float asum = 0.f;
-    if (!any_nan && lmax != -INFINITY)
-        for (int32_t i = 0; i < m.n_parts; ++i) {
-            float L = lp[i * m.l_part_stride];
-            if (L != -INFINITY) asum += expf(L - lmax);
+    const bool empty = (lmax == -INFINITY) || nan;
+    if (!empty)
+        for (int i = tid; i < m.n_parts; i += kThreads) {
+            const float L = lp[(int64_t)i * m.l_part_stride];
+            const float a = (L == -INFINITY) ? 0.f : expf(L - lmax);
+            if (i < kCachedWeights) s_w[i] = a;
+            asum += a;
         }
-    const int32_t n4 = m.Dv / 4;
-    const float inv = any_nan ? NAN : (asum > 0.f ? 1.f / asum : 0.f);
-    for (int32_t c = lane; c < n4; c += tpr) {
+    asum = block_reduce(asum, false, s_red);  // includes a barrier: s_w is visible
+
+    // 3. weighted column sums, parts spread over G thread groups
+    const int n4 = m.Dv / 4;
+    const int cols = n4 < kThreads ? n4 : kThreads;
+    const int G = kThreads / cols;
+    const int c0 = tid % cols, gi = tid / cols;
+    const float inv = nan ? NAN : (asum > 0.f ? 1.f / asum : 0.f);
+    for (int cb = 0; cb < n4; cb += cols) {
+        const int c = cb + c0;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (!any_nan && lmax != -INFINITY) {
-            for (int32_t i = 0; i < m.n_parts; ++i) {
-                float L = lp[i * m.l_part_stride];
-                if (L == -INFINITY) continue;  // empty part: weight 0, output not read
-                float a = expf(L - lmax);
-                const float4 o = *reinterpret_cast<const float4 *>(
-                    m.part_out + i * m.o_part_stride + row * m.o_row_stride + 4 * (int64_t)c);
-                acc.x += a * o.x;
-                acc.y += a * o.y;
-                acc.z += a * o.z;
-                acc.w += a * o.w;
+        if (!empty && gi < G && c < n4) {
+            const float *op = obase + 4 * (int64_t)c;
+            for (int i = gi; i < m.n_parts; i += G) {
+                float a;
+                if (i < kCachedWeights) {
+                    a = s_w[i];
+                } else {
+                    const float L = lp[(int64_t)i * m.l_part_stride];
+                    a = (L == -INFINITY) ? 0.f : expf(L - lmax);
+                }
+                if (a > 0.f) {  // an empty part's output is never read
+                    const float4 o =
+                        *reinterpret_cast<const float4 *>(op + (int64_t)i * m.o_part_stride);
+                    acc.x += a * o.x;
+                    acc.y += a * o.y;
+                    acc.z += a * o.z;
+                    acc.w += a * o.w;
+                }
             }
         }
-        acc.x *= inv;
-        acc.y *= inv;
-        acc.z *= inv;
-        acc.w *= inv;
-        if (kBf16Out) {
-            uint2 pk;
-            pk.x = pack_bf16x2(acc.x, acc.y);
-            pk.y = pack_bf16x2(acc.z, acc.w);
-            reinterpret_cast<uint2 *>(m.out)[row * n4 + c] = pk;
-        } else {
-            reinterpret_cast<float4 *>(m.out)[row * n4 + c] = acc;
+        s_acc[tid] = acc;
+        __syncthreads();
+        if (gi == 0 && c < n4) {
+            for (int g2 = 1; g2 < G; ++g2) {
+                const float4 o = s_acc[g2 * cols + c0];
+                acc.x += o.x;
+                acc.y += o.y;
+                acc.z += o.z;
+                acc.w += o.w;
+            }
+            acc.x *= inv;
+            acc.y *= inv;
+            acc.z *= inv;
+            acc.w *= inv;
+            if (kBf16Out) {
+                u32x2 pk;
+                pk.x = pack_bf16x2(acc.x, acc.y);
+                pk.y = pack_bf16x2(acc.z, acc.w);
+                reinterpret_cast<u32x2 *>(m.out)[row * n4 + c] = pk;
+            } else {
+                reinterpret_cast<float4 *>(m.out)[row * n4 + c] = acc;
+            }
         }
+        __syncthreads();
     }
-    if (m.lse_out && lane == 0)
-        m.lse_out[row] = any_nan ? NAN : (lmax == -INFINITY ? -INFINITY : lmax + logf(asum));
+    if (m.lse_out && tid == 0)
+        m.lse_out[row] = nan ? NAN : (lmax == -INFINITY ? -INFINITY : lmax + logf(asum));
+}
+
+}  // namespace
+
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
 }
 
 cp_status launch_merge(const MergeDesc &m, hipStream_t stream) {
     if (m.rows == 0) return CP_OK;
-    int32_t n4 = m.Dv / 4;
-    int32_t tpr = n4 < 256 ? n4 : 256;
-    int32_t rpb = 256 / tpr;
-    int64_t blocks = ceil_div(m.rows, rpb);
-    if (blocks > 0x7fffffff) return fail(CP_E_UNSUPPORTED, "merge: too many rows");
+    if (m.rows > 0x7fffffff) return fail(CP_E_UNSUPPORTED, "merge: too many rows");
     if (m.out_dt == CP_BF16)
-        hipLaunchKernelGGL(merge_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, m, tpr,
-                           rpb);
+        hipLaunchKernelGGL(merge_rows_kernel<true>, dim3((unsigned)m.rows), dim3(kThreads), 0,
+                           stream, m);
     else
-        hipLaunchKernelGGL(merge_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, m,
-                           tpr, rpb);
+        hipLaunchKernelGGL(merge_rows_kernel<false>, dim3((unsigned)m.rows), dim3(kThreads), 0,
+                           stream, m);
     return check_launch("lse merge");
 }
 

@@ -51,8 +51,8 @@ __global__ void slot_map_kernel(int32_t T, const int32_t *__restrict__ req,
     }
     // local index: I tokens per complete round before this one, plus the offset
     // inside the group
-    int64_t l = (int64_t)(group / N) * I + (t - (int64_t)group * I);
-    int64_t blk = l / bs;
+    const int32_t l = (group / N) * I + (t - group * I);  // l <= t, fits in 32 bits
+    const int32_t blk = l / bs;
     if (blk >= max_blocks) {
         slot_out[j] = CP_SLOT_INVALID;
         return;
@@ -60,27 +60,35 @@ __global__ void slot_map_kernel(int32_t T, const int32_t *__restrict__ req,
     slot_out[j] = (int64_t)block_table[(int64_t)b * bt_stride + blk] * bs + (l - blk * bs);
 }
 
-// One thread per 16-byte chunk of a token's rows (all heads).
-__global__ void cache_write_kernel(int64_t T, const int64_t *__restrict__ slot,
-                                   const uint4 *__restrict__ k, const uint4 *__restrict__ v,
-                                   int32_t n_heads, int32_t row_chunks, uint4 *__restrict__ k_cache,
-                                   uint4 *__restrict__ v_cache, int64_t num_slots, int32_t bs) {
-    const int64_t per_tok = (int64_t)n_heads * row_chunks;
-    const int64_t total = T * per_tok;
-    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * blockDim.x) {
-        int64_t j = idx / per_tok;
-        int64_t c = idx - j * per_tok;
-        int64_t s = slot[j];
-        if (s < 0 || s >= num_slots) continue;
-        int64_t h = c / row_chunks;
-        int64_t cc = c - h * row_chunks;
-        int64_t blk = s / bs;
-        int64_t off = s - blk * bs;
-        int64_t dst = ((blk * n_heads + h) * bs + off) * row_chunks + cc;
-        k_cache[dst] = k[idx];
-        if (v) v_cache[dst] = v[idx];
+// One thread per 16-byte chunk of a token's rows (all heads).  Index math is
+// 32-bit (the host splits launches so that a launch covers < 2^31 chunks);
+// slots are split into (block, offset) by a shift when bs is a power of two.
+__global__ void cache_write_kernel(int32_t T, const int64_t *__restrict__ slot,
+                                   const u32x4 *__restrict__ k, const u32x4 *__restrict__ v,
+                                   uint32_t n_heads, uint32_t row_chunks,
+                                   u32x4 *__restrict__ k_cache, u32x4 *__restrict__ v_cache,
+                                   int64_t num_slots, int32_t bs, int32_t bs_log2) {
+    const uint32_t per_tok = n_heads * row_chunks;
+    const uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
+    const uint32_t j = idx / per_tok;
+    if (j >= (uint32_t)T) return;
+    const uint32_t c = idx - j * per_tok;
+    const int64_t s = slot[j];
+    if (s < 0 || s >= num_slots) return;
+    const uint32_t h = c / row_chunks;
+    const uint32_t cc = c - h * row_chunks;
+    int64_t blk, off;
+    if (bs_log2 >= 0) {
+        blk = s >> bs_log2;
+        off = s & (bs - 1);
+    } else {
+        blk = s / bs;
+        off = s - blk * bs;
     }
+    const int64_t dst = ((blk * n_heads + h) * bs + off) * row_chunks + cc;
+    const int64_t src = (int64_t)j * per_tok + c;
+    k_cache[dst] = k[src];
+    if (v) v_cache[dst] = v[src];
 }
 
 }  // namespace cpattn
@@ -135,12 +143,24 @@ extern "C" cp_status cp_cache_write(int64_t T, const int64_t *slot, const void *
     if (!slot || !k || !k_cache) return fail(CP_E_INVALID, "cp_cache_write: NULL pointer");
     if (!aligned16(k) || !aligned16(k_cache) || (v && (!aligned16(v) || !aligned16(v_cache))))
         return fail(CP_E_INVALID, "cp_cache_write: data pointers must be 16-byte aligned");
-    int32_t row_chunks = (int32_t)(((int64_t)row_dim * eb) / 16);
-    int64_t total = T * n_kv_heads * row_chunks;
-    int64_t blocks = ceil_div(total, 256);
-    if (blocks > 65536 * 16) blocks = 65536 * 16;
-    hipLaunchKernelGGL(cache_write_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, T, slot,
-                       (const uint4 *)k, (const uint4 *)v, n_kv_heads, row_chunks,
-                       (uint4 *)k_cache, (uint4 *)v_cache, num_blocks * bs, bs);
+    const int32_t row_chunks = (int32_t)(((int64_t)row_dim * eb) / 16);
+    const int64_t per_tok = (int64_t)n_kv_heads * row_chunks;
+    if (per_tok > (1 << 20)) return fail(CP_E_UNSUPPORTED, "cp_cache_write: rows too wide");
+    int bs_log2 = -1;
+    if ((bs & (bs - 1)) == 0)
+        for (bs_log2 = 0; (1 << bs_log2) < bs; ++bs_log2) {
+        }
+    // launches of < 2^31 chunks each
+    const int64_t tok_per_launch = ((int64_t)1 << 30) / per_tok;
+    for (int64_t t0 = 0; t0 < T; t0 += tok_per_launch) {
+        const int32_t tn = (int32_t)(T - t0 < tok_per_launch ? T - t0 : tok_per_launch);
+        const int64_t total = (int64_t)tn * per_tok;
+        const u32x4 *kp = (const u32x4 *)k + t0 * per_tok;
+        const u32x4 *vp = v ? (const u32x4 *)v + t0 * per_tok : nullptr;
+        hipLaunchKernelGGL(cache_write_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
+                           stream, tn, slot + t0, kp, vp, (uint32_t)n_kv_heads,
+                           (uint32_t)row_chunks, (u32x4 *)k_cache, (u32x4 *)v_cache,
+                           num_blocks * bs, bs, bs_log2);
+    }
     return check_launch("cp_cache_write");
 }
