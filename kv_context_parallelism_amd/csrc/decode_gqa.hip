@@ -409,7 +409,7 @@ GqaPlan plan_gqa(const cp_gqa_args &a) {
         // (request, KV head) boundary, then a (first, count) table
         const int G = a.Hq / a.Hkv;
         pl.rows = true;
-        pl.waves = gqa_rows_waves();
+        pl.waves = gqa_rows_waves(a);
         const size_t slots = (size_t)pl.waves + (size_t)a.B * a.Hkv;
         pl.ws_bytes = slots * G * (a.D + 1) * sizeof(float) + (size_t)a.B * a.Hkv * 2 * 4 + 512;
         return pl;

@@ -29,6 +29,8 @@
 // tile's scores, its V after this tile's V product.
 #include <math.h>
 
+#include <type_traits>
+
 #include "internal.hpp"
 
 namespace cpattn {
@@ -39,10 +41,14 @@ constexpr int kWaves = 4;       // waves per workgroup
 constexpr int kTile = 32;       // tokens per tile = per scheduling chunk
 constexpr int kNG = kTile / 16; // 16-token groups per tile
 constexpr int kMaxB = 8192;     // requests handled by the in-LDS prefix sum
+// Register bound for the compiler: at least 2 workgroups per CU.  The number
+// actually resident (3 when the kernel needs <= 168 VGPRs) is queried at run
+// time and sets how many waves the schedule spreads the work over.
+constexpr int kMinWgPerCu = 2;
 
 struct RowParams {
     const gbyte *q, *kc, *vc;
-    const int32_t *bt, *len;
+    cint32 *bt, *len;
     int32_t B, Hq, Hkv, bs_log2, bt_stride;
     int64_t num_blocks;
     float qk_scale;   // softmax scale * log2(e)
@@ -180,7 +186,9 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
     // Waves actually scheduled: never more than there are chunks, so every
     // scheduled wave owns at least one chunk and the waves covering one
     // (request, head) are consecutive -- which makes its partial slots consecutive.
-    const int64_t R_tot = (int64_t)p.Hkv * s_pref[p.B];
+    // values read back from LDS are the same in every lane: keep them scalar
+    auto pref = [&](int i) -> int32_t { return __builtin_amdgcn_readfirstlane(s_pref[i]); };
+    const int64_t R_tot = (int64_t)p.Hkv * pref(p.B);
     const int64_t W = R_tot < p.W ? R_tot : p.W;
 
     // ---- workgroup 0 publishes (first slot, count) of every (request, head) ----
@@ -211,16 +219,17 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
         int lo_b = 0, hi_b = p.B;  // largest b with Hkv * pref[b] <= cc
         while (hi_b - lo_b > 1) {
             const int mid = (lo_b + hi_b) >> 1;
-            if ((int64_t)p.Hkv * s_pref[mid] <= cc) lo_b = mid;
+            if ((int64_t)p.Hkv * pref(mid) <= cc) lo_b = mid;
             else hi_b = mid;
         }
         const int b = __builtin_amdgcn_readfirstlane(lo_b);
-        const int32_t n = s_pref[b + 1] - s_pref[b];
+        const int32_t pb = pref(b);
+        const int32_t n = pref(b + 1) - pb;
         if (n == 0) {  // only reachable through empty requests sharing a prefix value
             // (the search returns the last b with that prefix, which has n > 0)
             break;
         }
-        const int64_t rem = cc - (int64_t)p.Hkv * s_pref[b];
+        const int64_t rem = cc - (int64_t)p.Hkv * pb;
         const int g = (int)(rem / n);
         const int32_t k = (int32_t)(rem - (int64_t)g * n);
         const int32_t nseg = (int32_t)min<int64_t>(hi - cc, n - k);
@@ -231,7 +240,7 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
         const int32_t s1 = min(s0 + nseg * kTile, L);
         const int64_t slot = w + (int64_t)b * p.Hkv + g;
         const int h0 = g * G;
-        const int32_t *bt_row = p.bt + (int64_t)b * p.bt_stride;
+        cint32 *bt_row = p.bt + (int64_t)b * p.bt_stride;
 
         // ---- query chunk c of the G heads (lane-private) ----
         u32x4 qraw[G];
@@ -247,45 +256,27 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
             }
         }
 
-        // ---- block-table window: lane i holds the block of local block win0+i ----
-        int32_t win0 = s0 >> p.bs_log2;
-        int32_t bt_win = 0;
-        auto load_window = [&](int32_t first_blk) {
-            win0 = first_blk;
-            const int32_t last_needed = s1 > 0 ? (s1 - 1) >> p.bs_log2 : -1;
-            const int32_t blk = first_blk + lane;
-            int32_t v = 0;
-            if (blk <= last_needed) {
-                v = bt_row[blk];
-                if (v < 0 || (int64_t)v >= p.num_blocks) {
-                    bad = true;
-                    v = 0;
-                }
-            }
-            bt_win = v;
-        };
-        if (s1 > s0) load_window(win0);
-
-        // first cache row (head g) of the 16-token group at local index lb; groups
-        // past the segment's end map to its first group so addresses stay valid
+        // First cache row (head g) of the 16-token group at local index lb.  The
+        // block id is a uniform (scalar) load, so waiting for it never waits for
+        // the K/V vector loads in flight.  Groups past the segment's end map to
+        // its first group so that every address stays inside the cache.
         auto group_row = [&](int32_t lb) -> int64_t {
             const int32_t gsel = lb < s1 ? lb : s0;
-            int32_t idx = (gsel >> p.bs_log2) - win0;
-            if (idx >= 64) {  // uniform: move the window forward
-                load_window(gsel >> p.bs_log2);
-                idx = 0;
-            }
-            const int32_t phys = __builtin_amdgcn_readlane(bt_win, idx);
+            int32_t phys = bt_row[gsel >> p.bs_log2];
+            const bool ok = phys >= 0 && (int64_t)phys < p.num_blocks;
+            bad |= !ok;
+            phys = ok ? phys : 0;
             return ((int64_t)phys * p.Hkv + g) * bs + (gsel & (bs - 1));
         };
-        auto load_tile = [&](const gbyte *base, int32_t tb, u32x4 (&reg)[kNG][4]) {
+        auto load_tile = [&](const gbyte *base, const int64_t (&rows)[kNG], u32x4 (&reg)[kNG][4]) {
 #pragma unroll
             for (int gi = 0; gi < kNG; ++gi) {
-                const gbyte *gp = base + group_row(tb + gi * 16) * 256 + lane * 16;
+                const gbyte *gp = base + rows[gi] * 256 + lane * 16;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) reg[gi][j] = load16(gp + j * 1024);
             }
         };
+        int64_t rows_cur[kNG], rows_next[kNG];
 
         float m[NF], lpart[NF], acc[G][EPC];
 #pragma unroll
@@ -298,19 +289,32 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
 #pragma unroll
             for (int e = 0; e < EPC; ++e) acc[hh][e] = 0.f;
 
+        // q has arrived before the first K/V request: the loop is then entered
+        // with the same loads in flight from the prologue and from its back
+        // edge (K then V of one tile), so the waits inside stay exact.
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         u32x4 kreg[kNG][4], vreg[kNG][4];
         if (s1 > s0) {
-            load_tile(p.kc, s0, kreg);
-            load_tile(p.vc, s0, vreg);
+#pragma unroll
+            for (int gi = 0; gi < kNG; ++gi) rows_cur[gi] = group_row(s0 + gi * 16);
+            load_tile(p.kc, rows_cur, kreg);
+            load_tile(p.vc, rows_cur, vreg);
         }
-        for (int32_t tb = s0; tb < s1; tb += kTile) {
+        // One tile.  kTail: the segment's last tile is partial -- scores of
+        // tokens past the end become -inf and their V rows (which may hold NaN
+        // poison) are zeroed right before the V product.  Full tiles carry no
+        // masking at all, so no wait on the V loads is forced before the scores.
+        auto tile = [&](int32_t tb, auto tail_tag) {
+            constexpr bool kTail = decltype(tail_tag)::value;
             const int32_t tn = tb + kTile;
-            if (tn > s1) {  // last, partial tile: V rows past the end may hold NaN poison
+            // Block ids of the next tile, early: they are needed after the scores.
+            // Full tiles always prefetch (past the segment's end the rows clamp to
+            // its first group and the reads hit the cache): a conditional
+            // prefetch would make the compiler copy the live V registers, which
+            // forces a wait on every load in flight.
+            if constexpr (!kTail) {
 #pragma unroll
-                for (int gi = 0; gi < kNG; ++gi)
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        if (tb + gi * 16 + j * 4 + R >= s1) vreg[gi][j] = zero4;
+                for (int gi = 0; gi < kNG; ++gi) rows_next[gi] = group_row(tn + gi * 16);
             }
 
             // ---- scores: partial dots, then reduce-scatter over the row ----
@@ -334,12 +338,12 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
                     }
                 row_reduce_scatter<NV>(v, c);
                 // this lane's scores belong to token (c >> 2) of its row
-                const bool ok = (tb + gi * 16 + (c >> 2) * 4 + R) < s1;
+                const bool ok = !kTail || (tb + gi * 16 + (c >> 2) * 4 + R) < s1;
 #pragma unroll
                 for (int k2 = 0; k2 < NF; ++k2)
                     sc[gi][k2] = ok ? (kBf16 ? v[k2] * p.qk_scale : v[k2]) : -INFINITY;
             }
-            if (tn < s1) load_tile(p.kc, tn, kreg);
+            if constexpr (!kTail) load_tile(p.kc, rows_next, kreg);
 
             // ---- online softmax: max over the lanes holding the same head ----
             float alpha[NF];
@@ -406,6 +410,14 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
             }
             wave_sync();
 
+            if constexpr (kTail) {
+#pragma unroll
+                for (int gi = 0; gi < kNG; ++gi)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (tb + gi * 16 + j * 4 + R >= s1) vreg[gi][j] = zero4;
+            }
+
             // ---- V product ----
 #pragma unroll
             for (int gi = 0; gi < kNG; ++gi) {
@@ -445,8 +457,15 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
                     }
                 }
             }
-            if (tn < s1) load_tile(p.vc, tn, vreg);
-        }
+            if constexpr (!kTail) {
+                load_tile(p.vc, rows_next, vreg);
+#pragma unroll
+                for (int gi = 0; gi < kNG; ++gi) rows_cur[gi] = rows_next[gi];
+            }
+        };
+        int32_t tb = s0;
+        for (; tb + kTile <= s1; tb += kTile) tile(tb, std::false_type{});
+        if (tb < s1) tile(tb, std::true_type{});
 
         // ---- finish the segment: full sums, normalise, write the partial ----
         bad = __ballot(bad) != 0;
@@ -509,7 +528,7 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
 template <int EB, int G>
 cp_status launch_rows(const RowParams &p, hipStream_t stream) {
     const int64_t blocks = ceil_div(p.W, kWaves);
-    hipLaunchKernelGGL((gqa_rows_kernel<EB, G, 2>), dim3((unsigned)blocks), dim3(64 * kWaves), 0,
+    hipLaunchKernelGGL((gqa_rows_kernel<EB, G, kMinWgPerCu>), dim3((unsigned)blocks), dim3(64 * kWaves), 0,
                        stream, p);
     return check_launch("cp_decode_attn_partial_gqa");
 }
@@ -522,7 +541,35 @@ bool gqa_rows_supported(const cp_gqa_args &a) {
     return row256 && (G == 1 || G == 2 || G == 4 || G == 8) && a.B <= kMaxB;
 }
 
-int gqa_rows_waves() { return device_cus() * 2 * kWaves; }
+template <int EB, int G>
+int resident_wgs() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &n, reinterpret_cast<const void *>(gqa_rows_kernel<EB, G, kMinWgPerCu>),
+                64 * kWaves, 0) != hipSuccess ||
+            n < 1)
+            n = kMinWgPerCu;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+int gqa_rows_waves(const cp_gqa_args &a) {
+    const int G = a.Hq / a.Hkv;
+    int wg = kMinWgPerCu;
+    if (a.dt == CP_BF16) {
+        wg = G == 1 ? resident_wgs<2, 1>() : G == 2 ? resident_wgs<2, 2>()
+                   : G == 4 ? resident_wgs<2, 4>() : resident_wgs<2, 8>();
+    } else {
+        wg = G == 1 ? resident_wgs<4, 1>() : G == 2 ? resident_wgs<4, 2>()
+                   : G == 4 ? resident_wgs<4, 4>() : resident_wgs<4, 8>();
+    }
+    return device_cus() * wg * kWaves;
+}
 
 cp_status gqa_rows_launch(const cp_gqa_args &a, int bs_log2, float *ws_o, float *ws_l,
                           int32_t *seg, int32_t W, hipStream_t stream) {
@@ -530,8 +577,8 @@ cp_status gqa_rows_launch(const cp_gqa_args &a, int bs_log2, float *ws_o, float 
     p.q = to_global(a.q);
     p.kc = to_global(a.k_cache);
     p.vc = to_global(a.v_cache);
-    p.bt = a.block_table;
-    p.len = a.local_len;
+    p.bt = to_const(a.block_table);
+    p.len = to_const(a.local_len);
     p.B = a.B;
     p.Hq = a.Hq;
     p.Hkv = a.Hkv;

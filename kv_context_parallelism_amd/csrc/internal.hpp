@@ -79,7 +79,7 @@ int device_cus();
 
 // Row-layout GQA decode kernel (256-byte KV rows), decode_gqa_rows.hip.
 bool gqa_rows_supported(const cp_gqa_args &a);
-int gqa_rows_waves();
+int gqa_rows_waves(const cp_gqa_args &a);
 cp_status gqa_rows_launch(const cp_gqa_args &a, int bs_log2, float *ws_o, float *ws_l,
                           int32_t *seg, int32_t W, hipStream_t stream);
 
@@ -92,6 +92,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 inline gbyte *to_global(const void *p) { return (gbyte *)(p); }
+
+// Read-only metadata (block tables, lengths) read through the constant address
+// space: uniform reads of it become scalar loads, which wait on their own
+// counter instead of behind the KV vector loads in flight.
+#define CP_CONST __attribute__((address_space(4)))
+typedef const int32_t CP_CONST cint32;
+inline cint32 *to_const(const int32_t *p) { return (cint32 *)(p); }
 
 __device__ __forceinline__ u32x4 load16(gbyte *p) {
     return *reinterpret_cast<const CP_GLOBAL u32x4 *>(p);
