@@ -1,0 +1,132 @@
+"""GPU parity: PCP causal prefill -- each rank's two pieces against the chunk's
+own keys (causal), against every DCP shard of the cached prefix (paged), and the
+exact merge of the 1 + N partials -- compared with the fp64 oracle, which
+selects the rank's query rows with its own head-tail piece rule."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import cp_inputs as ci
+import kv_context_parallelism_amd as cp
+import oracle
+from _cases import announce, build_decode_case, gate_lowp, lowp_gate_passes
+
+pytestmark = pytest.mark.gpu
+ATOL_OUT, ATOL_LSE = 2e-2, 1e-3
+
+
+def _setup(C, P, N, Hq, Hkv, N_dcp, I, bs, seed):
+    """Chunk q/k/v (device, bf16) and the prefix held in N_dcp paged shards."""
+    D = 128
+    scale = 1 / math.sqrt(D)
+    q = ci.to_storage(ci.normal((C, Hq, D), seed + 1, "cuda"), "bf16")
+    k = ci.to_storage(ci.normal((C, Hkv, D), seed + 2, "cuda"), "bf16")
+    v = ci.to_storage(ci.normal((C, Hkv, D), seed + 3, "cuda"), "bf16")
+    wp = ci.Workload("prefix", "gqa_decode", B=1, Hq=Hq, Hkv=Hkv, D=D, Dv=D, N=N_dcp, I=I, bs=bs,
+                     q_dtype="bf16", kv_dtype="bf16", scale=scale, seed=seed + 50)
+    prefix = build_decode_case(wp, seq=[P], check_cache=P < 100000)
+    return q, k, v, prefix, scale
+
+
+def _rank_partials(q, k, v, prefix, P, r, N, scale):
+    """Causal partial + one partial per prefix shard, stacked [1 + N_dcp][2c][Hq][D]."""
+    outs, lses = [], []
+    o, l = cp.pcp_prefill_attn_causal(q, P, r, N, scale, k=k, v=v)
+    outs.append(o)
+    lses.append(l)
+    for sh in prefix.shards:
+        o, l = cp.pcp_prefill_attn_causal(q, P, r, N, scale, k_cache=sh["kc"], v_cache=sh["vc"],
+                                          block_table=sh["bt_dev"][0].contiguous(),
+                                          local_len=int(sh["ll"][0]))
+        outs.append(o)
+        lses.append(l)
+    po = torch.stack([x.reshape(-1, x.shape[-2], x.shape[-1]) for x in outs])
+    pl = torch.stack([x.reshape(-1, x.shape[-1]) for x in lses])
+    return po, pl
+
+
+def _oracle_rows(q, k, v, prefix, P, rows, scale, key_begin=None, key_end=None, shard=None,
+                 heads=None):
+    """fp64 oracle for chunk rows `rows` over the logical [prefix; chunk] keys."""
+    kall = np.concatenate([ci.bits(prefix.k.cpu()), ci.bits(k.cpu())])
+    vall = np.concatenate([ci.bits(prefix.v.cpu()), ci.bits(v.cpu())])
+    qb = ci.bits(q.cpu())[rows]
+    kb = P + rows if key_begin is None else key_begin
+    ke = P + rows + 1 if key_end is None else key_end
+    return oracle.attention(qb, kall, vall, key_begin=kb, key_end=ke, scale=scale, q_dtype="bf16",
+                            kv_dtype="bf16", shard=shard, heads=heads)
+
+
+@pytest.mark.parametrize("C,P,N,Hq,Hkv,N_dcp", [(256, 200, 2, 32, 8, 3), (384, 0, 3, 8, 8, 1),
+                                                 (512, 777, 4, 16, 8, 2), (256, 64, 2, 8, 1, 2)])
+def test_prefill_small(C, P, N, Hq, Hkv, N_dcp):
+    announce(f"prefill C={C} P={P} N={N} Hq={Hq} Hkv={Hkv} N_dcp={N_dcp}")
+    q, k, v, prefix, scale = _setup(C, max(P, 1), N, Hq, Hkv, N_dcp, 16, 16, 4000 + C + P)
+    if P == 0:
+        # an empty prefix: shards hold nothing; keep one real key out of the way
+        prefix.shards = []
+    Pk = prefix.k.shape[0] if P > 0 else 0
+    for r in range(N):
+        rows = oracle.pcp_rank_positions(C, N, r)
+        po, pl = _rank_partials(q, k, v, prefix, Pk, r, N, scale)
+        mo, ml = cp.cp_lse_merge(po, pl)
+        torch.cuda.synchronize()
+        po, pl, mo, ml = po.cpu().numpy(), pl.cpu().numpy(), mo.cpu().numpy(), ml.cpu().numpy()
+        if P == 0:
+            kall = ci.bits(k.cpu())
+            vall = ci.bits(v.cpu())
+            ro, rl = oracle.attention(ci.bits(q.cpu())[rows], kall, vall, key_begin=0,
+                                      key_end=rows + 1, scale=scale, q_dtype="bf16",
+                                      kv_dtype="bf16")
+            gate_lowp(po[0], ro, f"causal r{r}", ATOL_OUT)
+            gate_lowp(pl[0], rl, f"causal lse r{r}", ATOL_LSE, norm=None)
+            continue
+        ro, rl = _oracle_rows(q, k, v, prefix, Pk, rows, scale, key_begin=Pk + 0 * rows)
+        gate_lowp(po[0], ro, f"causal r{r}", ATOL_OUT)
+        gate_lowp(pl[0], rl, f"causal lse r{r}", ATOL_LSE, norm=None)
+        for s in range(N_dcp):
+            ro, rl = _oracle_rows(q, k, v, prefix, Pk, rows, scale, key_begin=0, key_end=Pk,
+                                  shard=(N_dcp, 16, s))
+            gate_lowp(po[1 + s], ro, f"prefix shard {s} r{r}", ATOL_OUT)
+            gate_lowp(pl[1 + s], rl, f"prefix lse shard {s} r{r}", ATOL_LSE, norm=None)
+        ro, rl = _oracle_rows(q, k, v, prefix, Pk, rows, scale, key_begin=0)
+        gate_lowp(mo, ro, f"merged r{r}", ATOL_OUT)
+        gate_lowp(ml, rl, f"merged lse r{r}", ATOL_LSE, norm=None)
+
+
+def test_prefill_full_workload_sampled():
+    w = ci.WORKLOADS["pcp_prefill_bf16"]
+    announce(f"{w.name}: C={w.C} P={w.P} N={w.N}, sampled rows")
+    q, k, v, prefix, scale = _setup(w.C, w.P, w.N, w.Hq, w.Hkv, w.N, w.I, w.bs, w.seed)
+    rng = np.random.default_rng(w.seed)
+    for r in [0, 5, 7]:
+        rows = oracle.pcp_rank_positions(w.C, w.N, r)
+        po, pl = _rank_partials(q, k, v, prefix, w.P, r, w.N, scale)
+        mo, ml = cp.cp_lse_merge(po, pl)
+        torch.cuda.synchronize()
+        # the first and last row of each piece plus random ones
+        c = w.C // (2 * w.N)
+        pick = np.unique(np.concatenate([[0, c - 1, c, 2 * c - 1], rng.integers(0, 2 * c, 4)]))
+        heads = [0, 13, 31]
+        ro, rl = _oracle_rows(q, k, v, prefix, w.P, rows[pick], scale, key_begin=0, heads=heads)
+        gate_lowp(mo.cpu().numpy()[pick][:, heads], ro, f"merged r{r}", ATOL_OUT)
+        gate_lowp(ml.cpu().numpy()[pick][:, heads], rl, f"merged lse r{r}", ATOL_LSE, norm=None)
+        ro, rl = _oracle_rows(q, k, v, prefix, w.P, rows[pick], scale, key_begin=w.P, heads=heads)
+        gate_lowp(po[0].cpu().numpy()[pick][:, heads], ro, f"causal r{r}", ATOL_OUT)
+
+
+def test_prefill_negative_control_and_validation():
+    C, P, N = 256, 300, 2
+    q, k, v, prefix, scale = _setup(C, P, N, 32, 8, 2, 16, 16, 4500)
+    rows = oracle.pcp_rank_positions(C, N, 1)
+    # the wrong rank's pieces must not pass for rank 1
+    o, _ = cp.pcp_prefill_attn_causal(q, P, 0, N, scale, k=k, v=v)
+    ro, _ = _oracle_rows(q, k, v, prefix, P, rows, scale, key_begin=P)
+    assert not lowp_gate_passes(o.reshape(-1, 32, 128).cpu().numpy(), ro, ATOL_OUT)
+    o, _ = cp.pcp_prefill_attn_causal(q, P, 1, N, scale, k=k, v=v)
+    assert lowp_gate_passes(o.reshape(-1, 32, 128).cpu().numpy(), ro, ATOL_OUT)
+    # a chunk not aligned to 2N is rejected
+    with pytest.raises(cp.CpError, match="CP_E_INVALID"):
+        cp.pcp_prefill_attn_causal(q[:250].contiguous(), P, 0, N, scale, k=k, v=v)
