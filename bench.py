@@ -1,17 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the context-parallel attention hot path on one MI355X.
 
-Default workload: one DCP decode step of a GQA model, bf16, 32 requests with
-contexts uniform in [4K, 32K], 32 query / 8 KV heads, head dim 128, KV sharded
-over 8 simulated DCP ranks (interleave 16, block size 16).  One step =
+Default workload (--workload gqa_decode_bf16): one DCP decode step of a GQA
+model, bf16, 32 requests with contexts uniform in [4K, 32K], 32 query / 8 KV
+heads, head dim 128, KV sharded over 8 simulated DCP ranks (interleave 16,
+block size 16).  One step =
   for every rank r: cp_slot_map + cp_cache_write of the step's new tokens,
   for every rank r: cp_decode_attn_partial_gqa over shard r,
   then cp_lse_merge of the 8 partials.
-Inputs are synthetic (seeded), resident in HBM before timing starts.
+value = KV bytes the step reads / step time (GB/s).
 
-Prints ONE JSON line: metric, value (KV GB/s over the whole step), roofline of
-the dominant kernel (the shard decode partial; HIP events around each launch in
-the timed region) and the fp64 CPU oracle timed on a bounded sample.
+Other workloads, same step structure:
+  mla_decode_bf16   absorbed MLA, 64 requests x 64K context, 128 heads, latent
+                    576 / value 512, 8 shards (interleave 1, block 64)
+  mla_decode_fp8    the same with an fp8 E4M3 latent cache, 4 requests x 1M
+  pcp_prefill_bf16  a 32K chunk over a 64K prefix in 8 DCP shards; per PCP rank
+                    the causal call over the chunk, one call per prefix shard
+                    and the merge; the chunk's K/V is first written to the shards
+value = algorithmic FLOP (unmasked score + PV products) / step time (TFLOP/s).
+
+Inputs are synthetic (seeded), resident in HBM before timing starts.  Prints
+ONE JSON line: metric, value, the roofline of the dominant kernel (HIP events
+around each of its launches in the timed region, on the stream it runs on) and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -46,6 +57,8 @@ def _cpu_cores() -> int:
 # ---------------------------------------------------------------------------
 
 class GqaDecodeBench:
+    metric_unit = "GB/s"
+
     def __init__(self, w, dev="cuda"):
         import numpy as np
         import torch
@@ -109,7 +122,12 @@ class GqaDecodeBench:
             self.per_launch_bytes.append(int(sh["ll"].sum()) * kv_tok
                                          + self.q.numel() * self.q.element_size()
                                          + w.B * w.Hq * (w.D + 1) * 4)
-        self.events = None
+        self.work_step = self.kv_bytes_step
+        self.per_launch_work = self.per_launch_bytes
+        self.launches_per_step = w.N
+        self.dominant = list(range(w.N))
+        self.kernel_name = "cp_decode_attn_partial_gqa (attention + split combine)"
+        self.dtype = w.kv_dtype
 
     def step(self, ev=None):
         cp, w = self.cp, self.w
@@ -166,13 +184,267 @@ class GqaDecodeBench:
                 "interleave": w.I, "block_size": w.bs}
 
 
+
+# ---------------------------------------------------------------------------
+# MLA decode step (absorbed latent, bf16 or fp8 E4M3 cache)
+# ---------------------------------------------------------------------------
+
+class MlaDecodeBench:
+    metric_unit = "TFLOP/s"
+
+    def __init__(self, w, dev="cuda"):
+        import numpy as np
+        import torch
+
+        import cp_inputs as ci
+        import kv_context_parallelism_amd as cp
+
+        self.w, self.cp = w, cp
+        seq = np.full(w.B, w.ctx[0], dtype=np.int32)
+        self.seq = seq
+        total = int(seq.sum())
+        self.q = ci.to_storage(ci.normal((w.B, w.Hq, w.D), w.seed + 1, dev, w.q_std), w.q_dtype)
+        lat = ci.normal((total, w.D), w.seed + 2, dev, w.kv_std)
+        if w.kv_dtype == "fp8_e4m3fn":
+            self.lat, self.kv_scale = ci.fp8_quantize(lat)
+        else:
+            self.lat, self.kv_scale = ci.to_storage(lat, w.kv_dtype), 1.0
+        del lat
+        offs = np.concatenate([[0], np.cumsum(seq)]).astype(np.int64)
+        self.offs = offs
+        seq_d = torch.from_numpy(seq).to(dev)
+        req_ctx = torch.from_numpy(np.repeat(np.arange(w.B, dtype=np.int32), seq - 1)).to(dev)
+        pos_ctx = torch.arange(int(seq[0]) - 1, dtype=torch.int32, device=dev).repeat(w.B)
+        keep = torch.ones(total, dtype=torch.bool, device=dev)
+        last = torch.from_numpy(offs[1:] - 1).to(dev)
+        keep[last] = False
+        lat_ctx = self.lat[keep].contiguous()
+        self.lat_new = self.lat[last].contiguous()
+        self.req_new = torch.arange(w.B, dtype=torch.int32, device=dev)
+        self.pos_new = torch.from_numpy(seq - 1).to(dev)
+        self.shards = []
+        for r in range(w.N):
+            ll_d = cp.cp_local_seq_lens(seq_d, r, w.N, w.I)
+            ll = ll_d.cpu().numpy()
+            bt, pool = ci.block_tables((ll.astype(np.int64) + w.bs - 1) // w.bs, w.seed + 100 + r,
+                                       1.25)
+            bt_d = torch.from_numpy(bt).to(dev)
+            kc = torch.empty(pool, w.bs, w.D, dtype=self.lat.dtype, device=dev)
+            ci.nan_fill_(kc, w.kv_dtype)
+            slots = cp.cp_slot_map(req_ctx, pos_ctx, bt_d, r, w.N, w.I, w.bs)
+            cp.cp_cache_write(slots, lat_ctx, None, kc, None, w.bs)
+            out = torch.empty(w.B, w.Hq, w.Dv, dtype=torch.float32, device=dev)
+            lse = torch.empty(w.B, w.Hq, dtype=torch.float32, device=dev)
+            args = cp.mla_args(self.q, kc, bt_d, ll_d, w.scale, out, lse, Dv=w.Dv,
+                               kv_scale=self.kv_scale)
+            ws = torch.empty(cp.cp_workspace_bytes(cp.CP_OP_DECODE_MLA, args), dtype=torch.uint8,
+                             device=dev)
+            self.shards.append(dict(ll=ll, ll_d=ll_d, bt_d=bt_d, kc=kc, ws=ws,
+                                    slots=torch.empty(w.B, dtype=torch.int64, device=dev)))
+            del slots
+        del lat_ctx, req_ctx, pos_ctx, keep
+        self.part_out = torch.empty(w.N, w.B, w.Hq, w.Dv, dtype=torch.float32, device=dev)
+        self.part_lse = torch.empty(w.N, w.B, w.Hq, dtype=torch.float32, device=dev)
+        self.out = torch.empty(w.B, w.Hq, w.Dv, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(w.B, w.Hq, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        flop_tok = w.Hq * (w.D + w.Dv) * 2
+        self.work_step = int(seq.sum()) * flop_tok
+        self.per_launch_work = [int(sh["ll"].sum()) * flop_tok for sh in self.shards]
+        eb = self.lat.element_size()
+        self.per_launch_bytes = [int(sh["ll"].sum()) * w.D * eb + self.q.numel() * 2
+                                 + w.B * w.Hq * (w.Dv + 1) * 4 for sh in self.shards]
+        self.launches_per_step = w.N
+        self.dominant = list(range(w.N))
+        self.kernel_name = "cp_decode_attn_partial_mla (attention + split combine)"
+        self.dtype = "bf16"
+
+    def step(self, ev=None):
+        cp, w = self.cp, self.w
+        for r, sh in enumerate(self.shards):
+            cp.cp_slot_map(self.req_new, self.pos_new, sh["bt_d"], r, w.N, w.I, w.bs,
+                           out=sh["slots"])
+            cp.cp_cache_write(sh["slots"], self.lat_new, None, sh["kc"], None, w.bs)
+        for r, sh in enumerate(self.shards):
+            if ev is not None:
+                ev[r][0].record()
+            cp.cp_decode_attn_partial_mla(self.q, sh["kc"], sh["bt_d"], sh["ll_d"], w.scale,
+                                          Dv=w.Dv, kv_scale=self.kv_scale, out=self.part_out[r],
+                                          lse=self.part_lse[r], workspace=sh["ws"])
+            if ev is not None:
+                ev[r][1].record()
+        cp.cp_lse_merge(self.part_out, self.part_lse, out=self.out, lse_out=self.lse)
+
+    def cpu_baseline(self, budget_s=15.0):
+        """The fp64 oracle on the same workload: shard partials of request 0,
+        sixteen heads at a time, shard after shard, until the budget is spent."""
+        import cp_inputs as ci
+        import oracle
+
+        w = self.w
+        L = int(self.seq[0])
+        lat = ci.bits(self.lat[:L].cpu()).reshape(L, 1, w.D)
+        q = ci.bits(self.q[:1].cpu())
+        work, parts, t0 = 0, 0, time.perf_counter()
+        for r in range(w.N):
+            n_own = int(self.shards[r]["ll"][0])
+            for h0 in range(0, w.Hq, 16):
+                oracle.attention(q, lat, lat, key_begin=0, key_end=L, Dv=w.Dv, scale=w.scale,
+                                 q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, kv_scale=self.kv_scale,
+                                 shard=(w.N, w.I, r), heads=list(range(h0, h0 + 16)))
+                work += n_own * 16 * (w.D + w.Dv) * 2
+                parts += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return work / dt / 1e12, (f"request 0: {parts} shard-partial x 16-head blocks "
+                                  f"({parts * 16} of {w.N * w.Hq} shard-heads)")
+
+    def config(self):
+        w = self.w
+        return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "latent": w.D,
+                "value_dim": w.Dv, "context": int(self.seq[0]), "kv_dtype": w.kv_dtype,
+                "dcp_shards": w.N, "interleave": w.I, "block_size": w.bs}
+
+
+# ---------------------------------------------------------------------------
+# PCP prefill step: every rank's causal part + its prefix partials + merge
+# ---------------------------------------------------------------------------
+
+class PrefillBench:
+    metric_unit = "TFLOP/s"
+
+    def __init__(self, w, dev="cuda"):
+        import numpy as np
+        import torch
+
+        import cp_inputs as ci
+        import kv_context_parallelism_amd as cp
+
+        self.w, self.cp = w, cp
+        C, P = w.C, w.P
+        self.q = ci.to_storage(ci.normal((C, w.Hq, w.D), w.seed + 1, dev), "bf16")
+        self.k = ci.to_storage(ci.normal((C, w.Hkv, w.D), w.seed + 2, dev), "bf16")
+        self.v = ci.to_storage(ci.normal((C, w.Hkv, w.D), w.seed + 3, dev), "bf16")
+        pk = ci.to_storage(ci.normal((P, w.Hkv, w.D), w.seed + 52, dev), "bf16")
+        pv = ci.to_storage(ci.normal((P, w.Hkv, w.D), w.seed + 53, dev), "bf16")
+        self.pk, self.pv = pk, pv
+        tot = torch.tensor([P + C], dtype=torch.int32, device=dev)
+        pre = torch.tensor([P], dtype=torch.int32, device=dev)
+        req_p = torch.zeros(P, dtype=torch.int32, device=dev)
+        pos_p = torch.arange(P, dtype=torch.int32, device=dev)
+        self.req_c = torch.zeros(C, dtype=torch.int32, device=dev)
+        self.pos_c = torch.arange(P, P + C, dtype=torch.int32, device=dev)
+        self.shards = []
+        for s in range(w.N):
+            cap = cp.cp_local_seq_lens(tot, s, w.N, w.I).cpu().numpy()
+            ll = int(cp.cp_local_seq_lens(pre, s, w.N, w.I).cpu()[0])
+            bt, pool = ci.block_tables((cap.astype(np.int64) + w.bs - 1) // w.bs, w.seed + 100 + s,
+                                       1.25)
+            bt_d = torch.from_numpy(bt).to(dev)
+            kc = ci.nan_fill_(torch.empty(pool, w.Hkv, w.bs, w.D, dtype=torch.bfloat16,
+                                          device=dev), "bf16")
+            vc = ci.nan_fill_(torch.empty_like(kc), "bf16")
+            slots = cp.cp_slot_map(req_p, pos_p, bt_d, s, w.N, w.I, w.bs)
+            cp.cp_cache_write(slots, pk, pv, kc, vc, w.bs)
+            self.shards.append(dict(ll=ll, bt_d=bt_d, bt_row=bt_d[0].contiguous(), kc=kc, vc=vc,
+                                    slots=torch.empty(C, dtype=torch.int64, device=dev)))
+        c = C // (2 * w.N)
+        self.part_out = torch.empty(w.N + 1, 2 * c, w.Hq, w.D, dtype=torch.float32, device=dev)
+        self.part_lse = torch.empty(w.N + 1, 2 * c, w.Hq, dtype=torch.float32, device=dev)
+        self.out = torch.empty(w.N, 2 * c, w.Hq, w.D, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(w.N, 2 * c, w.Hq, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        causal = C * (C + 1) // 2
+        self.work_causal = causal * w.Hq * 4 * w.D
+        self.work_prefix = C * P * w.Hq * 4 * w.D
+        self.work_step = self.work_causal + self.work_prefix
+        # events bracket every launch: per rank one causal-chunk call, then one
+        # call per prefix shard; the prefix calls carry 80% of the work
+        self.launches_per_step = w.N * (w.N + 1)
+        self.dominant = [r * (w.N + 1) + 1 + s for r in range(w.N) for s in range(w.N)]
+        self.secondary = [r * (w.N + 1) for r in range(w.N)]
+        self.per_launch_work = [self.work_prefix / (w.N * w.N)]
+        self.secondary_work = self.work_causal / w.N
+        kv_tok = w.Hkv * w.D * 2 * 2
+        self.per_launch_bytes = [sum(sh["ll"] for sh in self.shards) * kv_tok / w.N / w.N
+                                 + (2 * C // (2 * w.N)) * w.Hq * w.D * (2 + 4)]
+        self.kernel_name = "pcp_prefill_attn_causal over one paged DCP prefix shard"
+        self.dtype = "bf16"
+
+    def step(self, ev=None):
+        cp, w = self.cp, self.w
+        # the chunk's new K/V into the DCP shards (positions P .. P+C-1)
+        for s, sh in enumerate(self.shards):
+            cp.cp_slot_map(self.req_c, self.pos_c, sh["bt_d"], s, w.N, w.I, w.bs, out=sh["slots"])
+            cp.cp_cache_write(sh["slots"], self.k, self.v, sh["kc"], sh["vc"], w.bs)
+        k = 0
+        for r in range(w.N):
+            if ev is not None:
+                ev[k][0].record()
+            cp.pcp_prefill_attn_causal(self.q, w.P, r, w.N, w.scale, k=self.k, v=self.v,
+                                       out=self.part_out[0], lse=self.part_lse[0])
+            if ev is not None:
+                ev[k][1].record()
+            k += 1
+            for s, sh in enumerate(self.shards):
+                if ev is not None:
+                    ev[k][0].record()
+                cp.pcp_prefill_attn_causal(self.q, w.P, r, w.N, w.scale, k_cache=sh["kc"],
+                                           v_cache=sh["vc"], block_table=sh["bt_row"],
+                                           local_len=sh["ll"], out=self.part_out[1 + s],
+                                           lse=self.part_lse[1 + s])
+                if ev is not None:
+                    ev[k][1].record()
+                k += 1
+            cp.cp_lse_merge(self.part_out, self.part_lse, out=self.out[r], lse_out=self.lse[r])
+
+    def cpu_baseline(self, budget_s=15.0):
+        import numpy as np
+
+        import cp_inputs as ci
+        import oracle
+
+        w = self.w
+        kall = np.concatenate([ci.bits(self.pk.cpu()), ci.bits(self.k.cpu())])
+        vall = np.concatenate([ci.bits(self.pv.cpu()), ci.bits(self.v.cpu())])
+        q = ci.bits(self.q.cpu())
+        rows = oracle.pcp_rank_positions(w.C, w.N, w.N - 1)
+        done, work, t0 = 0, 0, time.perf_counter()
+        for i in rows[::max(1, len(rows) // 64)]:
+            oracle.attention(q[i:i + 1], kall, vall, key_begin=0, key_end=w.P + i + 1,
+                             scale=w.scale, q_dtype="bf16", kv_dtype="bf16")
+            work += (w.P + int(i) + 1) * w.Hq * 4 * w.D
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return work / dt / 1e12, f"{done} query rows of rank {w.N - 1} (all {w.Hq} heads, full causal + prefix)"
+
+    def config(self):
+        w = self.w
+        return {"workload": w.name, "chunk": w.C, "prefix": w.P, "pcp_ranks": w.N,
+                "dcp_shards": w.N, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
+                "interleave": w.I, "block_size": w.bs}
+
+
+BENCHES = {"gqa_decode": GqaDecodeBench, "mla_decode": MlaDecodeBench,
+           "pcp_prefill": PrefillBench}
+BENCH_WORKLOADS = ["gqa_decode_bf16", "mla_decode_bf16", "mla_decode_fp8", "pcp_prefill_bf16"]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gqa_decode_bf16", choices=["gqa_decode_bf16"])
+    ap.add_argument("--workload", default="gqa_decode_bf16", choices=BENCH_WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of a workload, run a plain device copy of MIB MiB (the "
+                         "known-size reference that scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the N shards are simulated as separate buffers on a "
@@ -184,14 +456,25 @@ def main():
     import cp_inputs as ci
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": args.steps}), flush=True)
+        return
     w = ci.WORKLOADS[args.workload]
     print(f"[bench] setting up {w.name}", file=sys.stderr, flush=True)
-    bench = GqaDecodeBench(w)
+    bench = BENCHES[w.kind](w)
     for _ in range(args.warmup):
         bench.step()
     torch.cuda.synchronize()
+    n_ev = bench.launches_per_step
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(w.N)] for _ in range(args.steps)]
+           for _ in range(n_ev)] for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -200,26 +483,41 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
-    launch_ms = [e[0].elapsed_time(e[1]) for step in ev for e in step]
+    launch_ms = [step[k][0].elapsed_time(step[k][1]) for step in ev for k in bench.dominant]
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
-    avg_bytes = sum(bench.per_launch_bytes) / len(bench.per_launch_bytes)
-    achieved = avg_bytes / avg_launch_s / 1e9
-    value = bench.kv_bytes_step / (ms_step / 1e3) / 1e9
+    unit = bench.metric_unit
+    if unit == "GB/s":
+        scale_v, peak, bound = 1e9, HBM_PEAK_GBS, "hbm"
+    else:
+        scale_v, peak, bound = 1e12, BF16_PEAK_TFLOPS, "mfma"
+    avg_work = sum(bench.per_launch_work) / len(bench.per_launch_work)
+    achieved = avg_work / avg_launch_s / scale_v
+    value = bench.work_step / (ms_step / 1e3) / scale_v
+    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": None, "kernel": bench.kernel_name,
+            "avg_launch_us": round(avg_launch_s * 1e6, 2),
+            ("algorithmic_bytes_per_launch" if unit == "GB/s" else "algorithmic_flop_per_launch"):
+                int(avg_work)}
+    if unit != "GB/s":
+        avg_bytes = sum(bench.per_launch_bytes) / len(bench.per_launch_bytes)
+        roof["hbm_gbs"] = round(avg_bytes / avg_launch_s / 1e9, 2) if avg_bytes else None
+    if getattr(bench, "secondary", None):
+        sec_ms = [step[k][0].elapsed_time(step[k][1]) for step in ev for k in bench.secondary]
+        sec_s = sum(sec_ms) / len(sec_ms) / 1e3
+        roof["secondary"] = {"kernel": "pcp_prefill_attn_causal over the chunk's own keys",
+                             "avg_launch_us": round(sec_s * 1e6, 2),
+                             "achieved": round(bench.secondary_work / sec_s / scale_v, 2),
+                             "frac": round(bench.secondary_work / sec_s / scale_v / peak, 4)}
     line = {
-        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic", "config": bench.config(),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "cp_decode_attn_partial_gqa (attention + split combine)",
-                     "avg_launch_us": round(avg_launch_s * 1e6, 2),
-                     "algorithmic_bytes_per_launch": int(avg_bytes)},
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": bench.dtype,
+        "data": "synthetic", "config": bench.config(), "roofline": roof,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on a bounded sample", file=sys.stderr, flush=True)
         v, sample = bench.cpu_baseline()
-        line["cpu_baseline"] = {"value": round(v, 4), "unit": "GB/s", "cores": _cpu_cores(),
+        line["cpu_baseline"] = {"value": round(v, 6), "unit": unit, "cores": _cpu_cores(),
                                 "kind": "oracle", "sample": sample}
     print(json.dumps(line), flush=True)
 
