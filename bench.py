@@ -42,6 +42,31 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
 
+def _counted_traffic(workload: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary (FETCH_SIZE and WRITE_SIZE, each scaled by a plain copy of known
+    size), or None when there is none or the kernel's sources have changed
+    since the counters were taken."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", f"{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_t = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+    m_f = re.search(r"^kernel_sources: (.+)$", text, re.M)
+    m_h = re.search(r"^kernel_sources_sha256_16: ([0-9a-f]+)$", text, re.M)
+    if not (m_t and m_f and m_h):
+        return None
+    h = hashlib.sha256()
+    for f in sorted(m_f.group(1).split()):
+        h.update(f.encode())
+        with open(os.path.join(ROOT, "kv_context_parallelism_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return int(m_t.group(1)) if h.hexdigest()[:16] == m_h.group(1) else None
+
+
 def _cpu_cores() -> int:
     n = os.environ.get("OMP_NUM_THREADS")
     if n and n.isdigit():
@@ -494,7 +519,8 @@ def main():
     achieved = avg_work / avg_launch_s / scale_v
     value = bench.work_step / (ms_step / 1e3) / scale_v
     roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": None, "kernel": bench.kernel_name,
+            "frac": round(achieved / peak, 4), "traffic": _counted_traffic(w.name),
+            "kernel": bench.kernel_name,
             "avg_launch_us": round(avg_launch_s * 1e6, 2),
             ("algorithmic_bytes_per_launch" if unit == "GB/s" else "algorithmic_flop_per_launch"):
                 int(avg_work)}
