@@ -30,10 +30,18 @@ CFLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
+# Per-file additions.  decode_mla.hip: every accumulator of the MLA kernel
+# (outputs, scores) must stay in arch VGPRs, where the online-softmax rescale
+# can update them in place; the default heuristic puts MFMA accumulators in
+# AGPRs and then copies all of them to VGPRs and back on every tile.
+FILE_FLAGS = {
+    "decode_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def _compile(src: str, asm: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if asm:
         cmd[1:1] = ["-save-temps=obj"]
     r = subprocess.run(cmd, capture_output=True, text=True, cwd=BUILD)

@@ -9,23 +9,39 @@
 // Keys are the whole latent row (Dk = 576: 512 latent + 64 rope), values its
 // first Dv = 512 columns.
 //
-// Design (a dense contraction: 128 heads x 576 against every cached row):
-//   * one workgroup = H/16 waves, wave w owns query heads 16w .. 16w+15;
-//     all waves share each 32-token latent tile, staged once from HBM into a
-//     double-buffered LDS ring (rows padded to 1168 B: conflict-free reads);
+// Design (a dense contraction: up to 128 heads x 576 against every cached row):
+//   * one workgroup = 8 waves (two per SIMD), wave w owning query heads
+//     16w .. 16w+15; every latent tile staged in LDS feeds all 128 heads.  A
+//     wave's accumulators (16 x 512 fp32 outputs, 16 x 32 scores) and its
+//     queries fit its 256 VGPRs; the file is compiled with MFMA results in
+//     VGPRs so that the softmax rescale updates them in place;
+//   * 32-token latent tiles go HBM -> LDS by global_load_lds (no registers),
+//     triple-buffered: two tiles are in flight while the third is consumed.
+//     The copies are issued from inline asm and waited for with explicit
+//     vmcnt counts, so the compiler does not serialise them against the LDS
+//     reads of the tile being consumed;
+//   * LDS rows are unpadded (1152 bytes) with the 16-byte chunks of row t
+//     XOR-swizzled by (t / 2) % 8: both LDS read patterns below are free of
+//     bank conflicts;
 //   * scores S^T = C Q^T on v_mfma_f32_16x16x32_bf16 (A = latent rows from
-//     LDS, B = the wave's 16 queries, kept in registers for the segment);
-//   * online softmax in the exp2 domain; the score tile comes out of the MFMA
-//     already in the A-operand layout of the value product (token order is
-//     permuted identically on both operands, so no register shuffle);
-//   * values O = P V on the same MFMA with the V operand read straight from the
-//     row-major tile by ds_read_b64_tr_b16 (transposing LDS read), 16 value
-//     columns per instruction; the 16 x 512 fp32 output tile stays in registers;
-//   * fp8 E4M3 latent is widened to bf16 while being staged (exact), the
-//     per-tensor scale folded into the score scale and the output;
-//   * the same balanced flat schedule as the GQA kernel: exactly the resident
-//     workgroups, each taking an equal range of (request, 32-token tile) space;
-//     partials to slot wg + request, merged exactly afterwards.
+//     LDS, B = the wave's 16 queries, held in registers for the segment); the
+//     score tile comes out in the A-operand layout of the value product (the
+//     token order inside the 32-token k-step is permuted identically on both
+//     operands);
+//   * values O = P V with the V operand read by ds_read_b64_tr_b16 (transposing
+//     LDS read);
+//   * both products are software-pipelined by hand, three LDS operands ahead;
+//   * online softmax in the exp2 domain with a lazily updated reference
+//     maximum: the output is rescaled only when a tile's maximum exceeds the
+//     reference by more than 2^8, which keeps every probability <= 256 and the
+//     result exact up to rounding while skipping almost all rescales;
+//   * fp8 E4M3 latent lands in a raw ring and is widened to bf16 (exact) one
+//     tile ahead of its use; the per-tensor scale is folded into the score
+//     scale and the output;
+//   * the balanced flat schedule of the GQA kernel: exactly the resident
+//     workgroups, each taking an equal range of (request, 32-token tile)
+//     space; partials go to slot workgroup + request and are merged exactly
+//     afterwards.
 #include <math.h>
 
 #include <type_traits>
@@ -38,17 +54,30 @@ namespace {
 
 constexpr int kDk = 576, kDv = 512;
 constexpr int kT = 32;                  // tokens per tile / per scheduling chunk
-constexpr int kRowB = kDk * 2 + 16;     // LDS row stride in bytes (bf16 + pad)
+constexpr int kRowB = kDk * 2;          // LDS row: 1152 bytes = 72 chunks of 16
+constexpr int kRowC = kRowB / 16;
+constexpr int kTileB = kT * kRowB;      // 36,864 bytes
 constexpr int kKs = kDk / 32;           // 18 k-steps of the score MFMA
 constexpr int kVb = kDv / 16;           // 32 value-column blocks
 constexpr int kMaxB = 4096;
-constexpr int kMaxWaves = 8;            // 128 heads
+constexpr int kWaves = 8;               // 16 heads per wave, two waves per SIMD
+constexpr int kHeadsWg = 16 * kWaves;   // 128
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLazy = 8.f;            // rescale only past 2^8
+
+// copies per tile: bf16 goes straight into the tile (36 copies of 64 chunks),
+// fp8 into a raw ring (36 chunks per row, 18 copies)
+constexpr int kBfSlots = kT * kRowC / 64;        // 36
+constexpr int kRawSlots = kT * (kDk / 16) / 64;  // 18
+static_assert(kT * kRowC % 64 == 0 && kT * (kDk / 16) % 64 == 0, "whole 64-chunk copies");
+static_assert(kRowC % 8 == 0, "the chunk swizzle permutes aligned groups of 8");
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
 
 struct MlaParams {
     const gbyte *q, *kv;
@@ -57,7 +86,7 @@ struct MlaParams {
     int64_t num_blocks;
     float qk_scale;   // scale * kv_scale * log2(e)
     float v_scale;    // kv_scale (fp8) or 1
-    int32_t W;        // workgroups launched
+    int32_t W;        // tile ranges = workgroups launched
     float *ws_o;      // [slots][H][512]
     float *ws_l;      // [slots][H]
     int32_t *seg;     // [B][2]
@@ -77,19 +106,75 @@ __device__ __forceinline__ int64_t owner_of(int64_t c, int64_t R, int64_t W) {
     return ((c + 1) * W - 1) / R;
 }
 
+// Chunk c (16 bytes) of tile row t sits at chunk position c ^ swz(t) of the row.
+__device__ __forceinline__ int swz(int t) { return (t >> 1) & 7; }
+
+// The lane id, recomputed where it is used: keeps per-lane addresses from
+// being hoisted out of the tile loop and held in registers.
+__device__ __forceinline__ int lane_id_here() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
+// One 64-lane HBM -> LDS copy: lane i moves 16 bytes from `src` to LDS byte
+// lds + 16 i.  `lds` must be wave-uniform.  Issued from asm so that the
+// compiler's wait insertion does not tie later LDS reads to it; every reader
+// waits explicitly (vm_wait + barrier) before touching the destination.
+// (M0 is written here and read by nothing the compiler emits in this file.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(gbyte *src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds), "v"(src)
+                 : "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] at [15:14]).  Issued as
+// the builtin so that the compiler's own wait tracking sees it.
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Wave w issues the copies w, w + 4, ... of a tile: wait until at most one
+// (or two) further tiles' worth of this wave's copies is outstanding.
+template <int Slots>
+__device__ __forceinline__ void wait_all_but_one_tile(bool one_in_flight, int wave) {
+    constexpr int lo = Slots / kWaves, extra = Slots % kWaves;
+    if (!one_in_flight) vm_wait<0>();
+    else if (wave < extra) vm_wait<lo + 1>();
+    else vm_wait<lo>();
+}
+
+template <int Slots>
+__device__ __forceinline__ void wait_all_but_two_tiles(bool two, bool one, int wave) {
+    constexpr int lo = Slots / kWaves, extra = Slots % kWaves;
+    if (two) {
+        if (wave < extra) vm_wait<2 * (lo + 1)>();
+        else vm_wait<2 * lo>();
+    } else {
+        wait_all_but_one_tile<Slots>(one, wave);
+    }
+}
+
 template <bool kFp8>
-__global__ void __launch_bounds__(64 * kMaxWaves, 1) mla_kernel(MlaParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][kT * kRowB];
-    // fp8 only: raw rows as loaded (size 1 otherwise)
-    __shared__ __attribute__((aligned(16))) uint8_t s_raw[2][kFp8 ? kT * kDk : 16];
+__global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
+    constexpr int kBfBufs = kFp8 ? 2 : 3;
+    constexpr int kRawBufs = kFp8 ? 3 : 1;
+    __shared__ __attribute__((aligned(16))) uint8_t s_kv[kBfBufs][kTileB];
+    __shared__ __attribute__((aligned(16))) uint8_t s_raw[kRawBufs][kFp8 ? kT * kDk : 16];
     __shared__ int32_t s_pref[kMaxB + 1];
-    __shared__ int32_t s_wsum[kMaxWaves];
+    __shared__ int32_t s_wsum[kWaves];
 
     const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int G4 = lane >> 4, j16 = lane & 15;
+    const int range = blockIdx.x;
     const int h0 = wave * 16;
     const bool active = h0 < p.H;  // waves past H only help stage tiles
     const int64_t cap = (int64_t)p.bt_stride << p.bs_log2;
@@ -101,7 +186,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves, 1) mla_kernel(MlaParams p) {
         return (L + kT - 1) / kT;
     };
     {
-        const int per = (p.B + nthr - 1) / nthr;
+        const int per = (p.B + kThreads - 1) / kThreads;
         const int b0 = tid * per;
         int32_t run = 0;
         for (int i = 0; i < per && b0 + i < p.B; ++i) run += tiles_of(p.len[b0 + i]);
@@ -120,7 +205,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves, 1) mla_kernel(MlaParams p) {
             s_pref[b0 + i] = acc;
             acc += tiles_of(p.len[b0 + i]);
         }
-        if (tid == nthr - 1) s_pref[p.B] = base + incl;
+        if (tid == kThreads - 1) s_pref[p.B] = base + incl;
         __syncthreads();
     }
     auto pref = [&](int i) -> int32_t { return __builtin_amdgcn_readfirstlane(s_pref[i]); };
@@ -128,7 +213,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves, 1) mla_kernel(MlaParams p) {
     const int64_t W = R_tot < p.W ? R_tot : p.W;
 
     if (blockIdx.x == 0) {
-        for (int b = tid; b < p.B; b += nthr) {
+        for (int b = tid; b < p.B; b += kThreads) {
             const int64_t n = s_pref[b + 1] - s_pref[b];
             int32_t first = 0, count = 0;
             if (n > 0) {
@@ -141,10 +226,13 @@ __global__ void __launch_bounds__(64 * kMaxWaves, 1) mla_kernel(MlaParams p) {
             p.seg[2 * b + 1] = count;
         }
     }
-    const int64_t wg = blockIdx.x;
-    if (wg >= W || R_tot == 0) return;
-    int64_t cc = wg * R_tot / W;
-    const int64_t hi = (wg + 1) * R_tot / W;
+    if (range >= W || R_tot == 0) return;
+    int64_t cc = (int64_t)range * R_tot / W;
+    const int64_t hi = ((int64_t)range + 1) * R_tot / W;
+
+    // LDS byte addresses of the buffers (wave-uniform)
+    const uint32_t kv_lds = (uint32_t)(uintptr_t)(lds_u8 *)(&s_kv[0][0]);
+    const uint32_t raw_lds = (uint32_t)(uintptr_t)(lds_u8 *)(&s_raw[0][0]);
 
     while (cc < hi) {
         int lo_b = 0, hi_b = p.B;
@@ -163,224 +251,277 @@ __global__ void __launch_bounds__(64 * kMaxWaves, 1) mla_kernel(MlaParams p) {
         const int32_t L = bad ? 0 : Lraw;
         const int32_t s0 = k * kT;
         const int32_t s1 = min(s0 + nseg * kT, L);
-        const int64_t slot = wg + b;
+        const int32_t ntile = s1 > s0 ? (s1 - s0 + kT - 1) / kT : 0;
+        const int64_t slot = range + b;
         cint32 *bt_row = p.bt + (int64_t)b * p.bt_stride;
 
-        // ---- the wave's 16 queries as the B operand: Q[h0+j16][32ks + 8 G4 .. +8] ----
+        // ---- the wave's 16 queries as the B operand: Q[h0 + l % 16][32 ks + 8 (l / 16) .. +8] ----
+        // (lanes of heads past H load head H - 1: their columns of the score and
+        // output tiles are computed but never written)
         u32x4_t qb[kKs];
-        if (active) {
-            gbyte *qrow = p.q + ((int64_t)b * p.H + h0 + j16) * (kDk * 2) + G4 * 16;
+        {
+            const int hq = min(h0 + (lane & 15), p.H - 1);
+            gbyte *qrow = p.q + ((int64_t)b * p.H + hq) * (kDk * 2) + (lane >> 4) * 16;
 #pragma unroll
             for (int ks = 0; ks < kKs; ++ks) qb[ks] = load16(qrow + ks * 64);
         }
+        vm_wait<0>();  // the queries are in registers before any tile copy is issued
 
-        // ---- staging of one tile (all threads): latent rows -> bf16 rows in LDS ----
-        // block ids of the tile's tokens (bs >= 16: at most two blocks per tile)
-        auto tile_blocks = [&](int32_t tb, int64_t &r0, int64_t &r1) {
-            const int32_t lb0 = tb, lb1 = tb + 16;
-            auto row_of = [&](int32_t lb) -> int64_t {
-                const int32_t gsel = lb < s1 ? lb : s0;
-                int32_t phys = bt_row[gsel >> p.bs_log2];
+        // ---- tile copies (all waves) ----
+        // Cache rows of the tile's tokens: a 32-token tile spans at most two
+        // blocks (bs >= 16).  Tokens past the segment's end reuse the row of its
+        // last token (finite data; their probability is forced to 0).  Copy sl
+        // fills destination chunks 64 sl .. 64 sl + 63 of the tile; the source
+        // chunk of destination position p in row t is p ^ swz(t).
+        auto issue_tile = [&](int32_t it) {
+            const int32_t tb = s0 + it * kT;
+            const int32_t nval = min(kT, s1 - tb);
+            auto row_of = [&](int32_t tok) -> int64_t {
+                int32_t phys = bt_row[tok >> p.bs_log2];
                 const bool ok = phys >= 0 && (int64_t)phys < p.num_blocks;
                 bad |= !ok;
                 phys = ok ? phys : 0;
-                return ((int64_t)phys << p.bs_log2) + (gsel & (bs - 1));
+                return ((int64_t)phys << p.bs_log2) + (tok & (bs - 1));
             };
-            r0 = row_of(lb0);
-            r1 = row_of(lb1);
-        };
-        // Tiles reach LDS without passing through registers: each lane of a
-        // global_load_lds_dwordx4 moves 16 bytes to LDS address base + 16 * lane,
-        // so lane (slot, lane) fetches the source chunk that belongs at LDS chunk
-        // c = 64 * slot + lane of the destination region.
-        //   bf16: the destination is the padded tile itself (73 chunks per row,
-        //         the 73rd is padding and not loaded);
-        //   fp8:  raw rows (36 chunks each) land in a staging ring and are
-        //         widened to bf16 after the tile has arrived.
-        auto stage_issue = [&](int32_t tb, int buf) {
-            int64_t r0, r1;
-            tile_blocks(tb, r0, r1);
-            constexpr int kPer = kFp8 ? kDk / 16 : kRowB / 16;   // chunks per destination row
-            constexpr int kSlots = (kT * kPer + 63) / 64;        // 64-chunk load instructions
-            uint8_t *base = kFp8 ? s_raw[buf] : s_kv[buf];
+            const int64_t r0 = row_of(tb);
+            const int64_t r1 = row_of(tb + min(16, nval - 1));  // == r0 + 16 within one block
+            if constexpr (kFp8) {
+                const uint32_t dst = raw_lds + (uint32_t)((it % 3) * (kT * kDk));
 #pragma unroll
-            for (int i = 0; i < (kSlots + kMaxWaves - 1) / kMaxWaves; ++i) {
-                const int sl = wave + kMaxWaves * i;
-                if (sl >= kSlots) break;
-                const int c = sl * 64 + lane;
-                const int tt = c / kPer, ch = c - tt * kPer;
-                const bool ok = tt < kT && (kFp8 || ch < kDk * 2 / 16) && tb + tt < s1;
-                if (ok) {
-                    const int64_t row = tt < 16 ? r0 + tt : r1 + (tt - 16);
-                    __builtin_amdgcn_global_load_lds(
-                        (const CP_GLOBAL void *)(p.kv + row * (kFp8 ? kDk : kDk * 2) + ch * 16),
-                        (__attribute__((address_space(3))) void *)(base + sl * 1024), 16, 0, 0);
+                for (int i = 0; i < (kRawSlots + kWaves - 1) / kWaves; ++i) {
+                    const int sl = wave + kWaves * i;
+                    if (sl >= kRawSlots) break;
+                    const int c = sl * 64 + lane_id_here();
+                    const int tt = min(c / (kDk / 16), nval - 1), ch = c % (kDk / 16);
+                    const int64_t row = (tt < 16 ? r0 : r1 - 16) + tt;
+                    dma16(p.kv + row * kDk + ch * 16,
+                          __builtin_amdgcn_readfirstlane(dst + sl * 1024));
+                }
+            } else {
+                const uint32_t dst = kv_lds + (uint32_t)((it % 3) * kTileB);
+#pragma unroll
+                for (int i = 0; i < (kBfSlots + kWaves - 1) / kWaves; ++i) {
+                    const int sl = wave + kWaves * i;
+                    if (sl >= kBfSlots) break;
+                    const int c = sl * 64 + lane_id_here();  // destination chunk in the tile
+                    const int t = c / kRowC, pos = c - t * kRowC;
+                    const int tt = min(t, nval - 1);
+                    const int64_t rbase = tt < 16 ? r0 : r1 - 16;
+                    dma16(p.kv + (rbase + tt) * kRowB + (pos ^ swz(t)) * 16,
+                          __builtin_amdgcn_readfirstlane(dst + sl * 1024));
                 }
             }
         };
-        // After the tile's loads have landed (vmcnt(0) + barrier): fp8 rows are
-        // widened into the bf16 tile; rows past the segment's end are zeroed (their
-        // probability is 0, and the V product must not see stale NaN bits).
-        auto stage_finish = [&](int32_t tb, int buf) {
-            uint8_t *dst = s_kv[buf];
+        // fp8: widen raw tile `it` into bf16 buffer it % 2 (all threads)
+        auto widen_tile = [&](int32_t it) {
             if constexpr (kFp8) {
-                const uint8_t *raw = s_raw[buf];
-                for (int c = tid; c < kT * (kDk / 16); c += nthr) {
-                    const int tt = c / (kDk / 16), ch = c - tt * (kDk / 16);
-                    u32x4_t lo = {0u, 0u, 0u, 0u}, hi2 = {0u, 0u, 0u, 0u};
-                    if (tb + tt < s1) {
-                        const u32x4_t x = *reinterpret_cast<const u32x4_t *>(raw + c * 16);
+                const uint8_t *raw = s_raw[it % 3];
+                uint8_t *dst = s_kv[it % 2];
+                for (int c = tid; c < kT * (kDk / 16); c += kThreads) {
+                    const int tt = c / (kDk / 16), ch = c % (kDk / 16);
+                    const u32x4_t x = *reinterpret_cast<const u32x4_t *>(raw + c * 16);
+                    u32x4_t lo, hi2;
 #pragma unroll
-                        for (int wd = 0; wd < 4; ++wd) {
-                            const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(x[wd], false);
-                            const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(x[wd], true);
-                            const uint32_t a = (__float_as_uint(f01[0]) >> 16) |
-                                               (__float_as_uint(f01[1]) & 0xffff0000u);
-                            const uint32_t b2 = (__float_as_uint(f23[0]) >> 16) |
-                                                (__float_as_uint(f23[1]) & 0xffff0000u);
-                            if (wd < 2) {
-                                lo[2 * wd] = a;
-                                lo[2 * wd + 1] = b2;
-                            } else {
-                                hi2[2 * (wd - 2)] = a;
-                                hi2[2 * (wd - 2) + 1] = b2;
-                            }
+                    for (int wd = 0; wd < 4; ++wd) {
+                        const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(x[wd], false);
+                        const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(x[wd], true);
+                        const uint32_t a = (__float_as_uint(f01[0]) >> 16) |
+                                           (__float_as_uint(f01[1]) & 0xffff0000u);
+                        const uint32_t b2 = (__float_as_uint(f23[0]) >> 16) |
+                                            (__float_as_uint(f23[1]) & 0xffff0000u);
+                        if (wd < 2) {
+                            lo[2 * wd] = a;
+                            lo[2 * wd + 1] = b2;
+                        } else {
+                            hi2[2 * (wd - 2)] = a;
+                            hi2[2 * (wd - 2) + 1] = b2;
                         }
                     }
-                    *reinterpret_cast<u32x4_t *>(dst + tt * kRowB + ch * 32) = lo;
-                    *reinterpret_cast<u32x4_t *>(dst + tt * kRowB + ch * 32 + 16) = hi2;
-                }
-            } else if (tb + kT > s1) {
-                const u32x4_t z = {0u, 0u, 0u, 0u};
-                for (int c = tid; c < kT * (kDk * 2 / 16); c += nthr) {
-                    const int tt = c / (kDk * 2 / 16), ch = c - tt * (kDk * 2 / 16);
-                    if (tb + tt >= s1) *reinterpret_cast<u32x4_t *>(dst + tt * kRowB + ch * 16) = z;
+                    *reinterpret_cast<u32x4_t *>(dst + tt * kRowB + ((2 * ch) ^ swz(tt)) * 16) = lo;
+                    *reinterpret_cast<u32x4_t *>(dst + tt * kRowB + ((2 * ch + 1) ^ swz(tt)) * 16) = hi2;
                 }
             }
         };
 
-        float m_run = -INFINITY, l_run = 0.f;  // stats of head h0 + j16 (same in all 4 groups)
+        float m_ref = -INFINITY, l_run = 0.f;  // per head lane % 16 (same in all four groups)
         f32x4_t o[kVb];
 #pragma unroll
         for (int vb = 0; vb < kVb; ++vb) o[vb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        int buf = 0;
-        if (s1 > s0) stage_issue(s0, 0);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile has landed in LDS
-        __syncthreads();
-        if (s1 > s0) stage_finish(s0, 0);
-        if (kFp8 || s0 + kT > s1) __syncthreads();
-        for (int32_t tb = s0; tb < s1; tb += kT) {
-            const int32_t tn = tb + kT;
-            const bool has_next = tn < s1;  // uniform across the workgroup
-            // the next tile streams into the other buffer while this one is used
-            if (has_next) stage_issue(tn, buf ^ 1);
-            const uint8_t *tile = s_kv[buf];
-            if (active) {
-            // ---- scores S^T[t][h]: two 16-token halves ----
-            f32x4_t sc[2];
+        // Both products are software-pipelined by hand: the LDS operand of step
+        // i + kPre is requested before the MFMA of step i, and a scheduling
+        // barrier after each step keeps the compiler from hoisting further
+        // reads into registers.
+        constexpr int kPre = 3;
+        auto compute_tile = [&](int32_t it, const uint8_t *tile) {
+            const int32_t tb = s0 + it * kT;
+            // Per-lane LDS addresses (16-lane group G = lane / 16, j = lane % 16),
+            // recomputed per tile from a fresh lane id.  Score operand of half hf,
+            // k-step ks: row 16 hf + j, chunk 4 ks + G.  Value operand of column
+            // block vb: rows 4 G + j / 4 (and + 16), chunk 2 vb + (j % 4) / 2, byte
+            // 8 (j % 2).  Rows r and r + 16 share swz(r), so the + 16 row halves
+            // are a constant offset; the swizzle acts on the chunk's low 3 bits.
+            lds_u8 *t3 = (lds_u8 *)(tile);
+            lds_u8 *ap[2], *vp[4];
+            {
+                const int ln = lane_id_here();
+                const int G = ln >> 4, j = ln & 15;
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-                const uint8_t *arow = tile + (hf * 16 + j16) * kRowB + G4 * 16;
+                for (int k2 = 0; k2 < 2; ++k2) ap[k2] = t3 + j * kRowB + 16 * ((4 * k2 + G) ^ swz(j));
+                const int vr = 4 * G + (j >> 2);
 #pragma unroll
-                for (int ks = 0; ks < kKs; ++ks) {
-                    const u32x4_t a = *reinterpret_cast<const u32x4_t *>(arow + ks * 64);
-                    acc = mfma16(a, qb[ks], acc);
-                }
-                sc[hf] = acc;
+                for (int v4 = 0; v4 < 4; ++v4)
+                    vp[v4] = t3 + vr * kRowB + 16 * ((2 * v4 + ((j & 3) >> 1)) ^ swz(vr)) + 8 * (j & 1);
             }
-            // lane holds tokens tb + 16 hf + 4 G4 + e of head h0 + j16
+            auto read_a = [&](int i) -> u32x4_t {  // step i: half i % 2, k-step i / 2
+                const int hf = i & 1, ks = i >> 1;
+                return *(__attribute__((address_space(3))) const u32x4_t *)(
+                    ap[ks & 1] + hf * 16 * kRowB + 128 * (ks >> 1));
+            };
+            auto read_v = [&](int vb) -> u32x4_t {
+                lds_u8 *va = vp[vb & 3] + 128 * (vb >> 2);
+                const i16x4_t t0 =
+                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t *)(va));
+                const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(va + 16 * kRowB));
+                const u32x2_t w0 = __builtin_bit_cast(u32x2_t, t0), w1 = __builtin_bit_cast(u32x2_t, t1);
+                return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
+            };
+
+            // ---- scores S^T[t][h]: two 16-token halves x 18 k-steps, the halves
+            // interleaved (two independent accumulation chains) ----
+            f32x4_t sc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+            {
+                constexpr int kSteps = 2 * kKs;
+                u32x4_t abuf[kPre];
+#pragma unroll
+                for (int i = 0; i < kPre; ++i) abuf[i] = read_a(i);
+#pragma unroll
+                for (int i = 0; i < kSteps; ++i) {
+                    const u32x4_t a = abuf[i % kPre];
+                    if (i + kPre < kSteps) abuf[i % kPre] = read_a(i + kPre);
+                    sc[i & 1] = mfma16(a, qb[i >> 1], sc[i & 1]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
+            // lane holds head lane % 16, tokens tb + 16 hf + 4 G + e
+            const int G = lane >> 4;
+            const int lim = s1 - tb - 4 * G;  // token (hf, e) is real iff 16 hf + e < lim
             float mt = -INFINITY;
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     float s = sc[hf][e] * p.qk_scale;
-                    if (tb + hf * 16 + G4 * 4 + e >= s1) s = -INFINITY;
+                    if (16 * hf + e >= lim) s = -INFINITY;
                     sc[hf][e] = s;
                     mt = fmaxf(mt, s);
                 }
             mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
             mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-            const float mn = fmaxf(m_run, mt);
-            const float alpha = fast_exp2(m_run - mn);
-            m_run = mn;
+            if (it == 0) {
+                m_ref = mt;
+            } else if (__any(mt > m_ref + kLazy)) {
+                const float mn = fmaxf(m_ref, mt);
+                const float alpha = fast_exp2(m_ref - mn);
+                m_ref = mn;
+                l_run *= alpha;
+                // output row e of this lane is head 4 G + e
+                const int gb = (lane_id_here() >> 4) * 4;
+                float ar[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ar[e] = __shfl(alpha, gb + e, 64);
+#pragma unroll
+                for (int vb = 0; vb < kVb; ++vb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[vb][e] *= ar[e];
+            }
             float ps = 0.f;
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    sc[hf][e] = fast_exp2(sc[hf][e] - mn);
+                    sc[hf][e] = fast_exp2(sc[hf][e] - m_ref);
                     ps += sc[hf][e];
                 }
-            l_run = l_run * alpha + ps;  // partial over this lane's tokens
-            // P as the A operand: k = 8 G4 + e <-> tokens 4 G4 + e (e < 4), 16 + 4 G4 + e - 4
+            l_run += ps;
+            // P as the A operand: k = 8 G + e <-> tokens 4 G + e (e < 4) and
+            // 16 + 4 G + e - 4
             u32x4_t pa;
             pa[0] = pack2_bf16(sc[0][0], sc[0][1]);
             pa[1] = pack2_bf16(sc[0][2], sc[0][3]);
             pa[2] = pack2_bf16(sc[1][0], sc[1][1]);
             pa[3] = pack2_bf16(sc[1][2], sc[1][3]);
-            // rescale the output rows (heads 4 G4 + e) by their alpha
-            float ar[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ar[e] = __shfl(alpha, G4 * 4 + e, 64);
-#pragma unroll
-            for (int vb = 0; vb < kVb; ++vb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[vb][e] *= ar[e];
 
             // ---- values: O[h][v] += P[h][t] V[t][v], 16 columns per MFMA ----
-            const uint8_t *vrow0 = tile + (4 * G4 + (j16 >> 2)) * kRowB + (j16 & 3) * 8;
-            const uint8_t *vrow1 = vrow0 + 16 * kRowB;
+            {
+                u32x4_t vbuf[kPre];
 #pragma unroll
-            for (int vb = 0; vb < kVb; ++vb) {
-                const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    LDS_PTR(i16x4_t, vrow0 + vb * 32));
-                const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    LDS_PTR(i16x4_t, vrow1 + vb * 32));
-                u32x4_t vbop;
-                vbop[0] = (uint32_t)(uint16_t)t0[0] | ((uint32_t)(uint16_t)t0[1] << 16);
-                vbop[1] = (uint32_t)(uint16_t)t0[2] | ((uint32_t)(uint16_t)t0[3] << 16);
-                vbop[2] = (uint32_t)(uint16_t)t1[0] | ((uint32_t)(uint16_t)t1[1] << 16);
-                vbop[3] = (uint32_t)(uint16_t)t1[2] | ((uint32_t)(uint16_t)t1[3] << 16);
-                o[vb] = mfma16(pa, vbop, o[vb]);
+                for (int i = 0; i < kPre; ++i) vbuf[i] = read_v(i);
+#pragma unroll
+                for (int vb = 0; vb < kVb; ++vb) {
+                    const u32x4_t v = vbuf[vb % kPre];
+                    if (vb + kPre < kVb) vbuf[vb % kPre] = read_v(vb + kPre);
+                    o[vb] = mfma16(pa, v, o[vb]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
-            }  // active
+        };
 
-            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next tile landed
-            __syncthreads();                     // and nobody reads this buffer any more
-            if (has_next) {
-                stage_finish(tn, buf ^ 1);
-                if (kFp8 || tn + kT > s1) __syncthreads();
+        if constexpr (kFp8) {
+            // raw ring of 3, bf16 double buffer; tile it + 1 is widened while
+            // tile it is consumed
+            if (ntile > 0) issue_tile(0);
+            if (ntile > 1) issue_tile(1);
+            if (ntile > 2) issue_tile(2);
+            wait_all_but_two_tiles<kRawSlots>(ntile > 2, ntile > 1, wave);
+            __syncthreads();
+            if (ntile > 0) widen_tile(0);
+            for (int32_t it = 0; it < ntile; ++it) {
+                // raw tile it + 1 has landed (tile it + 2 may still be in flight)
+                wait_all_but_one_tile<kRawSlots>(it + 2 < ntile, wave);
+                __syncthreads();  // widened tile it complete; buffers of it - 1 free
+                if (it + 3 < ntile) issue_tile(it + 3);
+                if (it + 1 < ntile) widen_tile(it + 1);
+                if (active) compute_tile(it, s_kv[it % 2]);
             }
-            buf ^= 1;
+        } else {
+            if (ntile > 0) issue_tile(0);
+            if (ntile > 1) issue_tile(1);
+            for (int32_t it = 0; it < ntile; ++it) {
+                wait_all_but_one_tile<kBfSlots>(it + 1 < ntile, wave);
+                __syncthreads();  // tile it landed for all waves; buffer of it - 1 free
+                if (it + 2 < ntile) issue_tile(it + 2);
+                if (active) compute_tile(it, s_kv[it % 3]);
+            }
         }
 
         // ---- finish: full softmax sums, normalise, write this segment's partial ----
         float lt = l_run;
         lt += __shfl_xor(lt, 16, 64);
         lt += __shfl_xor(lt, 32, 64);
-        bad = __syncthreads_or(bad);
-        const bool empty = !(s1 > s0);
-        float inv[4];
+        bad = __syncthreads_or(bad);  // also: every wave is done with the LDS ring
+        const bool empty = ntile == 0;
+        const float inv_h = bad ? NAN : (empty ? 0.f : p.v_scale / lt);
+        if (active) {
+            const int ln = lane_id_here();
+            const int gb = (ln >> 4) * 4, lc = ln & 15;
+            float *o_dst = p.ws_o + (slot * p.H + h0) * kDv + lc;
+            float iv[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float le = __shfl(lt, G4 * 4 + e, 64);
-            inv[e] = bad ? NAN : (empty ? 0.f : p.v_scale / le);
-        }
-        float *o_dst = p.ws_o + (slot * p.H + h0) * kDv;
-        if (active)
+            for (int e = 0; e < 4; ++e) iv[e] = __shfl(inv_h, gb + e, 64);
 #pragma unroll
-            for (int vb = 0; vb < kVb; ++vb)
+            for (int vb = 0; vb < kVb; ++vb) {
+                const f32x4_t ov = o[vb];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    o_dst[(G4 * 4 + e) * kDv + vb * 16 + j16] = o[vb][e] * inv[e];
-        if (active && lane < 16)
-            p.ws_l[slot * p.H + h0 + lane] =
-                bad ? NAN : (empty ? -INFINITY : (m_run + fast_log2(lt)) * kLn2);
+                    if (h0 + gb + e < p.H) o_dst[(gb + e) * kDv + vb * 16] = ov[e] * iv[e];
+            }
+            if (ln < 16 && h0 + ln < p.H)
+                p.ws_l[slot * p.H + h0 + ln] =
+                    bad ? NAN : (empty ? -INFINITY : (m_ref + fast_log2(lt)) * kLn2);
+        }
         cc += nseg;
-        __syncthreads();  // the LDS ring is reused by the next segment
     }
 }
 
@@ -413,10 +554,9 @@ int log2_exact(int32_t x) {
 MlaPlan plan_mla(const cp_mla_args &a) {
     MlaPlan pl{};
     const bool fp8 = a.kv_dt == CP_FP8_E4M3FN;
-    const int threads = 64 * kMaxWaves;
-    const int wgs = device_cus() * (fp8 ? resident_wgs<true>(threads) : resident_wgs<false>(threads));
+    const int wgs = device_cus() * (fp8 ? resident_wgs<true>(kThreads) : resident_wgs<false>(kThreads));
     pl.split_tokens = kT;
-    pl.nsplit = wgs;  // workgroups launched
+    pl.nsplit = wgs;  // tile ranges = workgroups launched
     const size_t slots = (size_t)wgs + (size_t)(a.B > 0 ? a.B : 0);
     pl.ws_bytes = slots * (size_t)a.H * (kDv + 1) * sizeof(float) + (size_t)a.B * 2 * 4 + 512;
     return pl;
@@ -437,7 +577,7 @@ extern "C" cp_status cp_decode_attn_partial_mla(const cp_mla_args *a, void *ws, 
     if (a->Dk != kDk || a->Dv != kDv)
         return fail(CP_E_UNSUPPORTED, "mla decode: latent %d / value %d (576 / 512 supported)",
                     a->Dk, a->Dv);
-    if (a->H % 16 != 0 || a->H > 16 * kMaxWaves)
+    if (a->H % 16 != 0 || a->H > 2 * kHeadsWg)
         return fail(CP_E_UNSUPPORTED, "mla decode: H=%d (a multiple of 16 up to 128)", a->H);
     if (a->kv_dt != CP_BF16 && a->kv_dt != CP_FP8_E4M3FN)
         return fail(CP_E_UNSUPPORTED, "mla decode: latent dtype must be BF16 or FP8_E4M3FN");
@@ -481,11 +621,10 @@ extern "C" cp_status cp_decode_attn_partial_mla(const cp_mla_args *a, void *ws, 
     p.ws_o = ws_o;
     p.ws_l = ws_l;
     p.seg = seg;
-    const int threads = 64 * kMaxWaves;
     if (fp8)
-        hipLaunchKernelGGL(mla_kernel<true>, dim3(pl.nsplit), dim3(threads), 0, stream, p);
+        hipLaunchKernelGGL(mla_kernel<true>, dim3(pl.nsplit), dim3(kThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL(mla_kernel<false>, dim3(pl.nsplit), dim3(threads), 0, stream, p);
+        hipLaunchKernelGGL(mla_kernel<false>, dim3(pl.nsplit), dim3(kThreads), 0, stream, p);
     cp_status st = check_launch("cp_decode_attn_partial_mla");
     if (st != CP_OK) return st;
 

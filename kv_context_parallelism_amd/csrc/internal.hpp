@@ -42,7 +42,7 @@ GqaPlan plan_gqa(const cp_gqa_args &a);
 
 struct MlaPlan {
     int32_t split_tokens;
-    int32_t nsplit;
+    int32_t nsplit;  // workgroups launched (partial slots besides the per-request ones)
     size_t ws_bytes;
 };
 MlaPlan plan_mla(const cp_mla_args &a);

@@ -46,6 +46,18 @@ def test_mla_bf16_ragged(H, bs, N, I):
     _check(case, range(4), range(N))
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_mla_sharp_softmax_rescales(fp8):
+    """Scores with a standard deviation of ~6 (scale 1/4 on unit-variance data):
+    the running maximum jumps by more than the kernel's lazy-rescale margin
+    many times within a segment, so the rescale path is exercised."""
+    base = ci.WORKLOADS["mla_decode_fp8" if fp8 else "mla_decode_bf16_peaked"]
+    w = ci.scaled(base, B=3, Hq=48, N=2, I=1, bs=64, scale=0.25, seed=3400 + fp8)
+    announce(f"mla sharp softmax fp8={fp8}")
+    case = build_decode_case(w, seq=[2500, 77, 4096])
+    _check(case, range(3), range(2))
+
+
 @pytest.mark.parametrize("seq", [[37, 1500], [64, 4097]])
 def test_mla_fp8_ragged(seq):
     w = ci.scaled(ci.WORKLOADS["mla_decode_fp8"], B=len(seq), N=2, seed=3200 + seq[0])
