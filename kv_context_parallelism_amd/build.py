@@ -30,12 +30,13 @@ CFLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
-# Per-file additions.  decode_mla.hip: every accumulator of the MLA kernel
+# Per-file additions.  decode_mla.hip, prefill.hip: every accumulator of the kernel
 # (outputs, scores) must stay in arch VGPRs, where the online-softmax rescale
 # can update them in place; the default heuristic puts MFMA accumulators in
 # AGPRs and then copies all of them to VGPRs and back on every tile.
 FILE_FLAGS = {
     "decode_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

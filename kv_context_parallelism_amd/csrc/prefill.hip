@@ -15,14 +15,24 @@
 // Design:
 //   * workgroup = G waves (the query heads of one KV head) x 32 query rows of
 //     one piece; every 64-key K/V tile staged in LDS serves all G heads;
-//   * K/V tiles go from HBM straight into a double-buffered, row-padded LDS
-//     ring (global_load_lds); scores S^T = K Q^T on v_mfma_f32_16x16x32_bf16
-//     with the wave's queries held in registers; the score tile is already in
-//     the A-operand layout of the value product; V is read by the transposing
-//     LDS read ds_read_b64_tr_b16;
-//   * online softmax in the exp2 domain; causal masking only on the diagonal
-//     tile (key position <= query position), tiles past the diagonal are never
-//     visited;
+//   * K/V tiles go from HBM straight into a double-buffered LDS ring
+//     (global_load_lds issued from asm and waited for with explicit vmcnt
+//     counts, so the copy of tile j + 1 overlaps the compute of tile j); the
+//     block ids of a tile are read once, by scalar loads;
+//   * LDS rows are unpadded (256 bytes) with the 16-byte chunks of row t
+//     XOR-swizzled by t % 16: the row-major score-operand reads and the
+//     transposing value reads are both free of bank conflicts;
+//   * scores S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with the wave's queries
+//     held in registers (each K read feeds both 16-row blocks, eight
+//     independent accumulation chains interleaved); the score tile is already
+//     in the A-operand layout of the value product; V is read by the
+//     transposing LDS read ds_read_b64_tr_b16; LDS operands are requested
+//     three steps ahead of their MFMA;
+//   * online softmax in the exp2 domain with a lazily raised reference
+//     maximum (rescale only past 2^8); causal masking only on tiles that
+//     straddle the diagonal (key position <= query position), tiles past the
+//     diagonal are never visited; keys past the visible range reuse the last
+//     visible row (finite data) and get probability 0;
 //   * blockIdx % Hkv is the KV head, so the workgroups reading one head's keys
 //     share an XCD (and its L2); query blocks are issued longest-first.
 #include <math.h>
@@ -36,15 +46,18 @@ namespace {
 constexpr int kD = 128;
 constexpr int kBM = 32;                  // query rows per workgroup
 constexpr int kBN = 64;                  // keys per tile
-constexpr int kRowB = kD * 2 + 16;       // padded LDS row (272 B)
-constexpr int kTileB = kBN * kRowB;      // one K or V tile in LDS
+constexpr int kRowB = kD * 2;            // LDS row (256 B = 16 chunks)
+constexpr int kTileB = kBN * kRowB;      // one K or V tile in LDS (16 KB)
+constexpr int kSlots = 2 * kTileB / 1024;  // 64-lane copies per K+V tile pair (32)
 constexpr int kMaxWaves = 8;
+constexpr float kLazy = 8.f;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T *)(p))
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
 
 struct PrefillParams {
     const gbyte *q;
@@ -69,14 +82,35 @@ __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
            ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(hi)) << 16);
 }
 
+// The lane id, recomputed where it is used: keeps per-lane addresses from
+// being hoisted out of the tile loop and held in registers.
+__device__ __forceinline__ int lane_id_here() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
+// One 64-lane HBM -> LDS copy: lane i moves 16 bytes from `src` to LDS byte
+// lds + 16 i (`lds` wave-uniform).  Issued from asm so that the compiler's
+// wait insertion does not tie the LDS reads of the tile being consumed to it;
+// readers wait explicitly (vmcnt + barrier).  M0 is written here and read by
+// nothing the compiler emits in this file.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(gbyte *src, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds), "v"(src)
+                 : "m0");
+}
+#pragma clang diagnostic pop
+
 template <bool kPaged>
 __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_k[2][kTileB];
-    __shared__ __attribute__((aligned(16))) uint8_t s_v[2][kTileB];
+    __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][2 * kTileB];  // [buf][K tile | V tile]
 
     const int tid = threadIdx.x;
-    const int nthr = blockDim.x;
-    const int nwaves = nthr >> 6;
+    const int nwaves = blockDim.x >> 6;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int G4 = lane >> 4, j16 = lane & 15;
@@ -105,98 +139,125 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qb_reg[mb][ks] = load16(qrow + ks * 64);
     }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): queries in registers before any copy
 
     // ---- tile staging: 64 key rows of K and V straight into LDS ----
     bool bad = false;
-    auto key_row = [&](int32_t t, const gbyte *dense, const gbyte *paged) -> const gbyte * {
-        if constexpr (kPaged) {
-            int32_t phys = p.bt[t >> p.bs_log2];
-            const bool ok = phys >= 0 && (int64_t)phys < p.num_blocks;
-            bad |= !ok;
-            phys = ok ? phys : 0;
-            return paged + (((int64_t)phys * p.Hkv + g) * bs + (t & (bs - 1))) * (kD * 2);
-        } else {
-            return dense + ((int64_t)t * p.Hkv + g) * (kD * 2);
-        }
-    };
+    const uint32_t kv_lds = (uint32_t)(uintptr_t)(lds_u8 *)(&s_kv[0][0]);
     auto stage_issue = [&](int32_t j0, int buf) {
-        constexpr int kPer = kRowB / 16;              // 17 LDS chunks per row (16 data + pad)
-        constexpr int kSlots = (kBN * kPer + 63) / 64;
-        for (int sl = wave; sl < 2 * kSlots; sl += nwaves) {
-            const bool isv = sl >= kSlots;
-            const int s2 = isv ? sl - kSlots : sl;
-            const int cidx = s2 * 64 + lane;
-            const int tt = cidx / kPer, ch = cidx - tt * kPer;
-            // the row's physical block is uniform per 16 keys: read it once per row group
-            const bool ok = tt < kBN && ch < 16 && j0 + tt < kend;
-            if (ok) {
-                const gbyte *src = key_row(j0 + tt, isv ? p.v : p.k, isv ? p.vc : p.kc) + ch * 16;
-                uint8_t *dst = (isv ? s_v[buf] : s_k[buf]) + s2 * 1024;
-                __builtin_amdgcn_global_load_lds((const CP_GLOBAL void *)src,
-                                                 (__attribute__((address_space(3))) void *)dst, 16,
-                                                 0, 0);
+        // base row of each 16-key group of the tile (uniform: scalar loads)
+        int64_t base[4];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int32_t t = min(j0 + 16 * q4, kend - 1);
+            if constexpr (kPaged) {
+                int32_t phys = p.bt[t >> p.bs_log2];
+                const bool ok = phys >= 0 && (int64_t)phys < p.num_blocks;
+                bad |= !ok;
+                phys = ok ? phys : 0;
+                base[q4] = ((int64_t)phys * p.Hkv + g) * bs + (t & (bs - 1) & ~15);
+            } else {
+                base[q4] = (int64_t)(t & ~15) * p.Hkv + g;  // row index in units of D
             }
         }
-    };
-    // rows past the visible range are zeroed (probability 0 must not meet NaN bits)
-    auto stage_zero_tail = [&](int32_t j0, int buf) {
-        if (j0 + kBN <= kend) return;
-        const u32x4_t z = {0u, 0u, 0u, 0u};
-        for (int cidx = tid; cidx < kBN * 16; cidx += nthr) {
-            const int tt = cidx >> 4, ch = cidx & 15;
-            if (j0 + tt >= kend) {
-                *reinterpret_cast<u32x4_t *>(s_k[buf] + tt * kRowB + ch * 16) = z;
-                *reinterpret_cast<u32x4_t *>(s_v[buf] + tt * kRowB + ch * 16) = z;
-            }
+        const uint32_t dst = kv_lds + (uint32_t)(buf * 2 * kTileB);
+        for (int sl = wave; sl < kSlots; sl += nwaves) {
+            const bool isv = sl >= kSlots / 2;
+            const int ln = lane_id_here();
+            const int tt = (sl & (kSlots / 2 - 1)) * 4 + (ln >> 4);  // key row in the tile
+            const int pos = ln & 15;
+            // clamp past the visible range to the last visible key (probability 0)
+            const int tc = min(tt, kend - 1 - j0);
+            const int q4 = tc >> 4, r16 = tc & 15;
+            const int64_t b4 = q4 == 0 ? base[0] : q4 == 1 ? base[1] : q4 == 2 ? base[2] : base[3];
+            const int64_t row = kPaged ? b4 + r16 : b4 + (int64_t)r16 * p.Hkv;
+            const gbyte *src = (kPaged ? (isv ? p.vc : p.kc) : (isv ? p.v : p.k)) +
+                               row * (kD * 2) + ((pos ^ (tt & 15)) * 16);
+            dma16(src, __builtin_amdgcn_readfirstlane(dst + sl * 1024));
         }
     };
 
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
     f32x4_t o[2][8];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    int buf = 0;
-    if (kend > 0) stage_issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    constexpr int kPre = 3;
+    const int ntile = kend > 0 ? (kend + kBN - 1) / kBN : 0;
+    if (ntile > 0) stage_issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 landed (own copies)
     __syncthreads();
-    if (kend > 0 && kBN > kend) {
-        stage_zero_tail(0, 0);
-        __syncthreads();
-    }
-    for (int32_t j0 = 0; j0 < kend; j0 += kBN) {
-        const int32_t jn = j0 + kBN;
-        const bool has_next = jn < kend;
-        if (has_next) stage_issue(jn, buf ^ 1);
-        const uint8_t *tk = s_k[buf];
-        const uint8_t *tv = s_v[buf];
+    for (int32_t it = 0; it < ntile; ++it) {
+        const int32_t j0 = it * kBN;
+        const int buf = it & 1;
+        if (it + 1 < ntile) stage_issue(j0 + kBN, buf ^ 1);
+        lds_u8 *tk = (lds_u8 *)(&s_kv[buf][0]);
+        lds_u8 *tv = tk + kTileB;
 
-        // ---- scores S^T[key][row]: 4 key blocks x 2 row blocks ----
+        // per-lane addresses (fresh lane id per tile).  Score operand of key
+        // block kb, k-step ks: row 16 kb + j, chunk 4 ks + G; since rows
+        // 16 kb + j share the swizzle j, ks only flips the chunk bits 2..3.
+        // Value operand of column block db, key step s2: rows 32 s2 + 4 G + j / 4
+        // (and + 16), chunk 2 db + (j % 4) / 2, byte 8 (j % 2).
+        lds_u8 *ap[4], *vp[2];
+        {
+            const int ln = lane_id_here();
+            const int G = ln >> 4, j = ln & 15;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) ap[ks] = tk + j * kRowB + 16 * ((4 * ks + G) ^ j);
+            const int vr = 4 * G + (j >> 2);
+            vp[0] = tv + vr * kRowB + 8 * (j & 1);
+            vp[1] = tv + (vr + 16) * kRowB + 8 * (j & 1);
+        }
+        const int vr_sw = (4 * G4 + (j16 >> 2)) & 15;  // swizzle of both value rows
+        auto read_a = [&](int i) -> u32x4_t {  // step i: ks = i / 4, kb = i % 4
+            const int ks = i >> 2, kb = i & 3;
+            return *(__attribute__((address_space(3))) const u32x4_t *)(ap[ks] + kb * 16 * kRowB);
+        };
+        auto read_v = [&](int i) -> u32x4_t {  // step i: s2 = i / 8, db = i % 8
+            const int s2 = i >> 3, db = i & 7;
+            const int chunk = (2 * db + ((j16 & 3) >> 1)) ^ vr_sw;
+            lds_u8 *va0 = vp[0] + s2 * 32 * kRowB + chunk * 16;
+            lds_u8 *va1 = vp[1] + s2 * 32 * kRowB + chunk * 16;
+            const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t *)(va0));
+            const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) i16x4_t *)(va1));
+            const u32x2_t w0 = __builtin_bit_cast(u32x2_t, t0), w1 = __builtin_bit_cast(u32x2_t, t1);
+            return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
+        };
+
+        // ---- scores S^T[key][row]: 4 key blocks x 2 row blocks, k-step outer ----
         f32x4_t sc[2][4];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const uint8_t *arow = tk + (kb * 16 + j16) * kRowB + G4 * 16;
-            u32x4_t a[4];
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const u32x4_t *>(arow + ks * 64);
+            for (int kb = 0; kb < 4; ++kb) sc[mb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        {
+            u32x4_t abuf[kPre];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < kPre; ++i) abuf[i] = read_a(i);
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) acc = mfma16(a[ks], qb_reg[mb][ks], acc);
-                sc[mb][kb] = acc;
+            for (int i = 0; i < 16; ++i) {
+                const u32x4_t a = abuf[i % kPre];
+                if (i + kPre < 16) abuf[i % kPre] = read_a(i + kPre);
+                const int ks = i >> 2, kb = i & 3;
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) sc[mb][kb] = mfma16(a, qb_reg[mb][ks], sc[mb][kb]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         // lane holds keys j0 + 16 kb + 4 G4 + e for query row i0 + 16 mb + j16
         const bool diag = !kPaged && (j0 + kBN - 1 > i0);  // some key may follow some row
-        float alpha[2];
         u32x4_t pa[2][2];
+        bool need = false;
+        float mt[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
             const int qrow = i0 + 16 * mb + j16;
-            float mt = -INFINITY;
+            float m = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -205,15 +266,35 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
                     float s = sc[mb][kb][e] * p.qk_scale;
                     if (key >= kend || (diag && key > qrow)) s = -INFINITY;
                     sc[mb][kb][e] = s;
-                    mt = fmaxf(mt, s);
+                    m = fmaxf(m, s);
                 }
-            mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-            const float mn = fmaxf(m_run[mb], mt);
-            // a row with no visible key yet keeps m = -inf: use 0 as the shift
-            const float ms = mn == -INFINITY ? 0.f : mn;
-            alpha[mb] = fast_exp2(m_run[mb] - ms);
-            m_run[mb] = mn;
+            m = fmaxf(m, __shfl_xor(m, 16, 64));
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
+            mt[mb] = m;
+            need |= m > m_ref[mb] + kLazy;
+        }
+        if (__any(need)) {
+            // raise the reference maximum of the rows that need it and rescale
+            // their partial sums and output rows 16 mb + 4 G4 + e
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const float mn = mt[mb] > m_ref[mb] + kLazy ? mt[mb] : m_ref[mb];
+                const float alpha = m_ref[mb] == -INFINITY ? 0.f : fast_exp2(m_ref[mb] - mn);
+                m_ref[mb] = mn;
+                l_run[mb] *= alpha;
+                float ar[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ar[e] = __shfl(alpha, G4 * 4 + e, 64);
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[mb][db][e] *= ar[e];
+            }
+        }
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            // a row with no visible key yet keeps the reference at -inf: shift by 0
+            const float ms = m_ref[mb] == -INFINITY ? 0.f : m_ref[mb];
             float ps = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
@@ -222,7 +303,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
                     sc[mb][kb][e] = fast_exp2(sc[mb][kb][e] - ms);
                     ps += sc[mb][kb][e];
                 }
-            l_run[mb] = l_run[mb] * alpha[mb] + ps;
+            l_run[mb] += ps;
             // P as A operand for 32-key steps: k = 8 G4 + e <-> key blocks (2s, 2s+1)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
@@ -232,45 +313,24 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
                 pa[mb][s2][3] = pack2_bf16(sc[mb][2 * s2 + 1][2], sc[mb][2 * s2 + 1][3]);
             }
         }
-        // rescale output rows 16 mb + 4 G4 + e
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            float ar[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ar[e] = __shfl(alpha[mb], G4 * 4 + e, 64);
-#pragma unroll
-            for (int db = 0; db < 8; ++db)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o[mb][db][e] *= ar[e];
-        }
         // ---- values: O[row][d] += P[row][key] V[key][d] ----
+        {
+            u32x4_t vbuf[kPre];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            const uint8_t *vrow0 = tv + (32 * s2 + 4 * G4 + (j16 >> 2)) * kRowB + (j16 & 3) * 8;
-            const uint8_t *vrow1 = vrow0 + 16 * kRowB;
+            for (int i = 0; i < kPre; ++i) vbuf[i] = read_v(i);
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                const i16x4_t t0 =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4_t, vrow0 + db * 32));
-                const i16x4_t t1 =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(i16x4_t, vrow1 + db * 32));
-                u32x4_t vb;
-                vb[0] = (uint32_t)(uint16_t)t0[0] | ((uint32_t)(uint16_t)t0[1] << 16);
-                vb[1] = (uint32_t)(uint16_t)t0[2] | ((uint32_t)(uint16_t)t0[3] << 16);
-                vb[2] = (uint32_t)(uint16_t)t1[0] | ((uint32_t)(uint16_t)t1[1] << 16);
-                vb[3] = (uint32_t)(uint16_t)t1[2] | ((uint32_t)(uint16_t)t1[3] << 16);
+            for (int i = 0; i < 16; ++i) {
+                const u32x4_t vb = vbuf[i % kPre];
+                if (i + kPre < 16) vbuf[i % kPre] = read_v(i + kPre);
+                const int s2 = i >> 3, db = i & 7;
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb) o[mb][db] = mfma16(pa[mb][s2], vb, o[mb][db]);
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
 
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // the next tile has landed
-        __syncthreads();
-        if (has_next && jn + kBN > kend) {
-            stage_zero_tail(jn, buf ^ 1);
-            __syncthreads();
-        }
-        buf ^= 1;
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed (own copies)
+        __syncthreads();                     // ... for all waves; this buffer is free again
     }
 
     // ---- finish: normalise and write rows of this piece ----
@@ -297,8 +357,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
         if (lane < 16) {
             const int r = local0 + 16 * mb + lane;
             p.lse[((int64_t)piece_slot * c + r) * p.Hq + h] =
-                bad ? NAN : (m_run[mb] == -INFINITY ? -INFINITY
-                                                    : (m_run[mb] + fast_log2(lt)) * kLn2);
+                bad ? NAN : (m_ref[mb] == -INFINITY || !(lt > 0.f)
+                                 ? -INFINITY
+                                 : (m_ref[mb] + fast_log2(lt)) * kLn2);
         }
     }
 }
