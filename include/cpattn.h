@@ -227,8 +227,8 @@ typedef struct cp_prefill_args {
  *    AllGather-Q path; partials are then merged with cp_lse_merge.
  * Supported: D = 128, Hq/Hkv in {1, 2, 4, 8}, bf16.
  * Workspace: none needed (cp_workspace_bytes returns 0).
- * Errors: CP_E_INVALID (C % (2*pcp_size), rank, sizes, pointers),
- * CP_E_UNSUPPORTED. */
+ * Errors: CP_E_INVALID (C % (2*pcp_size), rank, sizes, pointers, a scale
+ * that is not positive and finite), CP_E_UNSUPPORTED. */
 cp_status pcp_prefill_attn_causal(const cp_prefill_args *args, void *workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 

@@ -97,11 +97,6 @@ __device__ __forceinline__ f32x4_t mfma16(const u32x4_t &a, const u32x4_t &b, co
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(lo)) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(hi)) << 16);
-}
-
 __device__ __forceinline__ int64_t owner_of(int64_t c, int64_t R, int64_t W) {
     return ((c + 1) * W - 1) / R;
 }
@@ -448,10 +443,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
             // P as the A operand: k = 8 G + e <-> tokens 4 G + e (e < 4) and
             // 16 + 4 G + e - 4
             u32x4_t pa;
-            pa[0] = pack2_bf16(sc[0][0], sc[0][1]);
-            pa[1] = pack2_bf16(sc[0][2], sc[0][3]);
-            pa[2] = pack2_bf16(sc[1][0], sc[1][1]);
-            pa[3] = pack2_bf16(sc[1][2], sc[1][3]);
+            pa[0] = pack_bf16x2(sc[0][0], sc[0][1]);
+            pa[1] = pack_bf16x2(sc[0][2], sc[0][3]);
+            pa[2] = pack_bf16x2(sc[1][0], sc[1][1]);
+            pa[3] = pack_bf16x2(sc[1][2], sc[1][3]);
 
             // ---- values: O[h][v] += P[h][t] V[t][v], 16 columns per MFMA ----
             {

@@ -77,11 +77,6 @@ __device__ __forceinline__ f32x4_t mfma16(const u32x4_t &a, const u32x4_t &b, co
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
-    return (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(lo)) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(hi)) << 16);
-}
-
 // The lane id, recomputed where it is used: keeps per-lane addresses from
 // being hoisted out of the tile loop and held in registers.
 __device__ __forceinline__ int lane_id_here() {
@@ -230,11 +225,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
         };
 
         // ---- scores S^T[key][row]: 4 key blocks x 2 row blocks, k-step outer ----
+        // (raw dot products; the scale is applied inside the exponent below)
         f32x4_t sc[2][4];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) sc[mb][kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         {
             u32x4_t abuf[kPre];
 #pragma unroll
@@ -245,33 +237,41 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
                 if (i + kPre < 16) abuf[i % kPre] = read_a(i + kPre);
                 const int ks = i >> 2, kb = i & 3;
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) sc[mb][kb] = mfma16(a, qb_reg[mb][ks], sc[mb][kb]);
+                for (int mb = 0; mb < 2; ++mb)
+                    sc[mb][kb] = mfma16(a, qb_reg[mb][ks],
+                                        ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : sc[mb][kb]);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // lane holds keys j0 + 16 kb + 4 G4 + e for query row i0 + 16 mb + j16
+        // lane holds keys j0 + 16 kb + 4 G4 + e for query row i0 + 16 mb + j16.
+        // Only tiles that reach past the visible keys or straddle the diagonal
+        // need a mask (a uniform test).
         const bool diag = !kPaged && (j0 + kBN - 1 > i0);  // some key may follow some row
+        if (diag || j0 + kBN > kend) {
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) {
+                const int lim = min(kend, diag ? i0 + 16 * mb + j16 + 1 : kend) - j0 - 4 * G4;
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (16 * kb + e >= lim) sc[mb][kb][e] = -INFINITY;
+            }
+        }
         u32x4_t pa[2][2];
         bool need = false;
         float mt[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-            const int qrow = i0 + 16 * mb + j16;
-            float m = -INFINITY;
+            float m = fmaxf(fmaxf(sc[mb][0][0], sc[mb][0][1]), fmaxf(sc[mb][0][2], sc[mb][0][3]));
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int key = j0 + 16 * kb + 4 * G4 + e;
-                    float s = sc[mb][kb][e] * p.qk_scale;
-                    if (key >= kend || (diag && key > qrow)) s = -INFINITY;
-                    sc[mb][kb][e] = s;
-                    m = fmaxf(m, s);
-                }
+            for (int kb = 1; kb < 4; ++kb)
+                m = fmaxf(m, fmaxf(fmaxf(sc[mb][kb][0], sc[mb][kb][1]),
+                                   fmaxf(sc[mb][kb][2], sc[mb][kb][3])));
             m = fmaxf(m, __shfl_xor(m, 16, 64));
             m = fmaxf(m, __shfl_xor(m, 32, 64));
-            mt[mb] = m;
-            need |= m > m_ref[mb] + kLazy;
+            mt[mb] = m * p.qk_scale;  // the scale is positive: max commutes with it
+            need |= mt[mb] > m_ref[mb] + kLazy;
         }
         if (__any(need)) {
             // raise the reference maximum of the rows that need it and rescale
@@ -293,24 +293,25 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
         }
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-            // a row with no visible key yet keeps the reference at -inf: shift by 0
+            // p = 2^(s * scale - m_ref); a row with no visible key yet keeps the
+            // reference at -inf and shifts by 0
             const float ms = m_ref[mb] == -INFINITY ? 0.f : m_ref[mb];
             float ps = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    sc[mb][kb][e] = fast_exp2(sc[mb][kb][e] - ms);
+                    sc[mb][kb][e] = fast_exp2(fmaf(sc[mb][kb][e], p.qk_scale, -ms));
                     ps += sc[mb][kb][e];
                 }
             l_run[mb] += ps;
             // P as A operand for 32-key steps: k = 8 G4 + e <-> key blocks (2s, 2s+1)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                pa[mb][s2][0] = pack2_bf16(sc[mb][2 * s2][0], sc[mb][2 * s2][1]);
-                pa[mb][s2][1] = pack2_bf16(sc[mb][2 * s2][2], sc[mb][2 * s2][3]);
-                pa[mb][s2][2] = pack2_bf16(sc[mb][2 * s2 + 1][0], sc[mb][2 * s2 + 1][1]);
-                pa[mb][s2][3] = pack2_bf16(sc[mb][2 * s2 + 1][2], sc[mb][2 * s2 + 1][3]);
+                pa[mb][s2][0] = pack_bf16x2(sc[mb][2 * s2][0], sc[mb][2 * s2][1]);
+                pa[mb][s2][1] = pack_bf16x2(sc[mb][2 * s2][2], sc[mb][2 * s2][3]);
+                pa[mb][s2][2] = pack_bf16x2(sc[mb][2 * s2 + 1][0], sc[mb][2 * s2 + 1][1]);
+                pa[mb][s2][3] = pack_bf16x2(sc[mb][2 * s2 + 1][2], sc[mb][2 * s2 + 1][3]);
             }
         }
         // ---- values: O[row][d] += P[row][key] V[key][d] ----
@@ -401,7 +402,8 @@ extern "C" cp_status pcp_prefill_attn_causal(const cp_prefill_args *a, void *ws,
                     kBM);
     if (a->kv_source != CP_KV_DENSE && a->kv_source != CP_KV_PAGED)
         return fail(CP_E_INVALID, "prefill: kv_source %d", a->kv_source);
-    if (!(a->scale == a->scale)) return fail(CP_E_INVALID, "prefill: scale is NaN");
+    if (!(a->scale > 0.f) || !(a->scale < INFINITY))
+        return fail(CP_E_INVALID, "prefill: the softmax scale must be positive and finite");
     if (a->C == 0) return CP_OK;
     if (!a->q || !a->out || !a->lse) return fail(CP_E_INVALID, "prefill: NULL pointer");
     PrefillParams p{};

@@ -113,3 +113,9 @@ def test_host_validation_rejects_bad_arguments():
     p = _lib.CpPrefillArgs(q=16, C=100, P=0, pcp_rank=0, pcp_size=8, Hq=32, Hkv=8, D=128,
                            scale=0.1, kv_source=0, k=16, v=16, out=16, lse=16)
     assert lib.pcp_prefill_attn_causal(ctypes.byref(p), None, 0, None) in (1, 2)
+    # prefill: the softmax scale must be positive and finite
+    p.C, p.pcp_size = 128, 2
+    for bad_scale in (0.0, -0.1, float("inf"), float("nan")):
+        p.scale = bad_scale
+        assert lib.pcp_prefill_attn_causal(ctypes.byref(p), None, 0, None) == 1
+        assert b"scale" in lib.cp_last_error()
