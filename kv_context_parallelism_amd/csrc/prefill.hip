@@ -263,11 +263,13 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
         float mt[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-            float m = fmaxf(fmaxf(sc[mb][0][0], sc[mb][0][1]), fmaxf(sc[mb][0][2], sc[mb][0][3]));
+            float m = fmaxf(sc[mb][0][0], sc[mb][0][1]);
+            m = fmaxf(m, fmaxf(sc[mb][0][2], sc[mb][0][3]));
 #pragma unroll
-            for (int kb = 1; kb < 4; ++kb)
-                m = fmaxf(m, fmaxf(fmaxf(sc[mb][kb][0], sc[mb][kb][1]),
-                                   fmaxf(sc[mb][kb][2], sc[mb][kb][3])));
+            for (int kb = 1; kb < 4; ++kb) {
+                m = fmaxf(m, fmaxf(sc[mb][kb][0], sc[mb][kb][1]));  // v_max3
+                m = fmaxf(m, fmaxf(sc[mb][kb][2], sc[mb][kb][3]));
+            }
             m = fmaxf(m, __shfl_xor(m, 16, 64));
             m = fmaxf(m, __shfl_xor(m, 32, 64));
             mt[mb] = m * p.qk_scale;  // the scale is positive: max commutes with it
@@ -296,6 +298,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
             // p = 2^(s * scale - m_ref); a row with no visible key yet keeps the
             // reference at -inf and shifts by 0
             const float ms = m_ref[mb] == -INFINITY ? 0.f : m_ref[mb];
+            // (the denominator is summed in fp32: the LSE needs more than the
+            // bf16 precision of the weights)
             float ps = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb)
