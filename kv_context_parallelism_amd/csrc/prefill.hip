@@ -156,19 +156,40 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
             }
         }
         const uint32_t dst = kv_lds + (uint32_t)(buf * 2 * kTileB);
-        for (int sl = wave; sl < kSlots; sl += nwaves) {
-            const bool isv = sl >= kSlots / 2;
-            const int ln = lane_id_here();
-            const int tt = (sl & (kSlots / 2 - 1)) * 4 + (ln >> 4);  // key row in the tile
-            const int pos = ln & 15;
-            // clamp past the visible range to the last visible key (probability 0)
-            const int tc = min(tt, kend - 1 - j0);
-            const int q4 = tc >> 4, r16 = tc & 15;
-            const int64_t b4 = q4 == 0 ? base[0] : q4 == 1 ? base[1] : q4 == 2 ? base[2] : base[3];
-            const int64_t row = kPaged ? b4 + r16 : b4 + (int64_t)r16 * p.Hkv;
-            const gbyte *src = (kPaged ? (isv ? p.vc : p.kc) : (isv ? p.v : p.k)) +
-                               row * (kD * 2) + ((pos ^ (tt & 15)) * 16);
-            dma16(src, __builtin_amdgcn_readfirstlane(dst + sl * 1024));
+        const int ln = lane_id_here();
+        const int l16 = ln >> 4, pos = ln & 15;
+        if (j0 + kBN <= kend) {
+            // full tile: copy sl holds rows 4 (sl % 16) .. +3, all in the 16-key
+            // group q4 = (sl % 16) / 4; the per-lane part of the address is
+            // row r16 = 4 (sl % 4) + lane / 16 of the group and chunk
+            // (lane % 16) ^ r16 of that row
+            constexpr int64_t kRow = kD * 2;
+            const int64_t rstride = kPaged ? kRow : (int64_t)p.Hkv * kRow;
+            for (int sl = wave; sl < kSlots; sl += nwaves) {
+                const bool isv = sl >= kSlots / 2;
+                const int s2 = sl & (kSlots / 2 - 1);
+                const int q4 = s2 >> 2;
+                const int64_t b4 = q4 == 0 ? base[0] : q4 == 1 ? base[1] : q4 == 2 ? base[2] : base[3];
+                const gbyte *gbase =
+                    (kPaged ? (isv ? p.vc : p.kc) : (isv ? p.v : p.k)) + b4 * kRow;  // uniform
+                const int r16 = 4 * (s2 & 3) + l16;
+                const uint32_t off = (uint32_t)(r16 * rstride) + (uint32_t)((pos ^ r16) * 16);
+                dma16(gbase + off, __builtin_amdgcn_readfirstlane(dst + sl * 1024));
+            }
+        } else {
+            for (int sl = wave; sl < kSlots; sl += nwaves) {
+                const bool isv = sl >= kSlots / 2;
+                const int tt = (sl & (kSlots / 2 - 1)) * 4 + l16;  // key row in the tile
+                // clamp past the visible range to the last visible key (probability 0)
+                const int tc = min(tt, kend - 1 - j0);
+                const int q4 = tc >> 4, r16 = tc & 15;
+                const int64_t b4 =
+                    q4 == 0 ? base[0] : q4 == 1 ? base[1] : q4 == 2 ? base[2] : base[3];
+                const int64_t row = kPaged ? b4 + r16 : b4 + (int64_t)r16 * p.Hkv;
+                const gbyte *src = (kPaged ? (isv ? p.vc : p.kc) : (isv ? p.v : p.k)) +
+                                   row * (kD * 2) + ((pos ^ (tt & 15)) * 16);
+                dma16(src, __builtin_amdgcn_readfirstlane(dst + sl * 1024));
+            }
         }
     };
 
