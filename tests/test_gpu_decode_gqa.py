@@ -90,8 +90,9 @@ def test_gqa_deterministic_and_workspace():
     w = ci.scaled(ci.WORKLOADS["gqa_decode_bf16"], B=3, seed=2300)
     case = build_decode_case(w, seq=[5000, 9000, 20000], check_cache=False)
     a1 = run_partials(case)
-    a2 = run_partials(case)
-    assert torch.equal(a1[0], a2[0]) and torch.equal(a1[1], a2[1])
+    for _ in range(8):  # the split combine sums the partials in slot order
+        a2 = run_partials(case)
+        assert torch.equal(a1[0], a2[0]) and torch.equal(a1[1], a2[1])
     sh = case.shards[0]
     out = torch.empty(3, w.Hq, w.D, device="cuda")
     lse = torch.empty(3, w.Hq, device="cuda")
@@ -171,3 +172,38 @@ def test_lse_merge_against_oracle():
     mo2, ml2 = cp.cp_lse_merge(po.cuda(), pl2.cuda())
     assert torch.isnan(mo2[7].cpu()).all() and torch.isnan(ml2[7].cpu())
     assert torch.equal(mo2[8], mo[8])
+
+
+def test_gqa_one_workspace_many_calls_and_long_request():
+    """One workspace reused across calls of different shapes, an empty request,
+    and a single long request whose (request, KV head) rows are split over
+    hundreds of waves (hundreds of partials in one exact merge)."""
+    w = ci.scaled(ci.WORKLOADS["gqa_decode_bf16"], B=1, seed=2500)
+    long_case = build_decode_case(w, seq=[300000], check_cache=False, check_slots=False)
+    w2 = ci.scaled(ci.WORKLOADS["gqa_decode_bf16"], B=5, seed=2501)
+    short_case = build_decode_case(w2, seq=[17, 40, 4000, 0, 9000], check_cache=False)
+    need = 0
+    for case in (long_case, short_case):
+        sh = case.shards[0]
+        a = cp.gqa_args(case.q, sh["kc"], sh["vc"], sh["bt_dev"], sh["ll_dev"], case.w.scale,
+                        torch.empty(case.w.B, case.w.Hq, case.w.D, device="cuda"),
+                        torch.empty(case.w.B, case.w.Hq, device="cuda"))
+        need = max(need, cp.cp_workspace_bytes(cp.CP_OP_DECODE_GQA, a))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ref = {}
+    for rep in range(3):
+        for name, case in (("long", long_case), ("short", short_case)):
+            sh = case.shards[0]
+            o, l = cp.cp_decode_attn_partial_gqa(case.q, sh["kc"], sh["vc"], sh["bt_dev"],
+                                                 sh["ll_dev"], case.w.scale, workspace=ws)
+            torch.cuda.synchronize()
+            if rep == 0:
+                ref[name] = (o.clone(), l.clone())
+            else:
+                assert torch.equal(o, ref[name][0]) and torch.equal(l, ref[name][1]), name
+    for name, case in (("long", long_case), ("short", short_case)):
+        o, l = ref[name]
+        for b in range(case.w.B):
+            ro, rl = oracle_request(case, b, shard=(case.w.N, case.w.I, 0))
+            gate_lowp(o[b].cpu().numpy(), ro, f"{name} out b{b}", 2e-2)
+            gate_lowp(l[b].cpu().numpy(), rl, f"{name} lse b{b}", 1e-3, norm=None)
