@@ -163,7 +163,8 @@ typedef struct cp_mla_args {
 /* Absorbed multi-head latent attention on one DCP shard: one latent KV row
  * per token shared by all H query heads ([P1] section 3 "MLA path", KV head
  * effectively 1; [P3] Deep Dive 6: local attention then exact merge).
- * Supported: Dk = 576, Dv = 512, bs a multiple of 16, H a multiple of 16.
+ * Supported: Dk = 576, Dv = 512, bs a power of two >= 16, H a multiple of 16 up to
+ * 128 (CP_E_UNSUPPORTED otherwise).
  * Bad lengths / block ids give NaN rows as for GQA.
  * Workspace: cp_workspace_bytes(CP_OP_DECODE_MLA, &args).
  * Errors: as cp_decode_attn_partial_gqa. */

@@ -572,7 +572,7 @@ extern "C" cp_status cp_decode_attn_partial_mla(const cp_mla_args *a, void *ws, 
     if (a->Dk != kDk || a->Dv != kDv)
         return fail(CP_E_UNSUPPORTED, "mla decode: latent %d / value %d (576 / 512 supported)",
                     a->Dk, a->Dv);
-    if (a->H % 16 != 0 || a->H > 2 * kHeadsWg)
+    if (a->H % 16 != 0 || a->H > kHeadsWg)
         return fail(CP_E_UNSUPPORTED, "mla decode: H=%d (a multiple of 16 up to 128)", a->H);
     if (a->kv_dt != CP_BF16 && a->kv_dt != CP_FP8_E4M3FN)
         return fail(CP_E_UNSUPPORTED, "mla decode: latent dtype must be BF16 or FP8_E4M3FN");

@@ -119,3 +119,20 @@ def test_host_validation_rejects_bad_arguments():
         p.scale = bad_scale
         assert lib.pcp_prefill_attn_causal(ctypes.byref(p), None, 0, None) == 1
         assert b"scale" in lib.cp_last_error()
+
+
+def test_mla_validation_rejects_unsupported_head_counts():
+    """The MLA kernel covers up to 128 heads (four waves of 32) in multiples of
+    16; other head counts are refused on the host, before any device call."""
+    lib = _lib.load()
+    a = _lib.CpMlaArgs(q=16, kv_cache=16, block_table=16, local_len=16, B=2, H=128, Dk=576,
+                       Dv=512, bs=64, bt_stride=8, num_blocks=64, scale=0.1, kv_dt=1, kv_scale=1.0,
+                       out=16, lse=16)
+    for bad_h in (144, 256, 24, 8):
+        a.H = bad_h
+        assert lib.cp_decode_attn_partial_mla(ctypes.byref(a), None, 0, None) == 2
+        assert b"H=" in lib.cp_last_error()
+    a.H, a.Dk = 128, 512
+    assert lib.cp_decode_attn_partial_mla(ctypes.byref(a), None, 0, None) == 2
+    a.Dk, a.bs = 576, 24
+    assert lib.cp_decode_attn_partial_mla(ctypes.byref(a), None, 0, None) == 2
