@@ -13,12 +13,14 @@
 //   partial output and LSE per key set.
 //
 // Design:
-//   * workgroup = G waves (the query heads of one KV head) x 32 query rows of
-//     one piece; every 64-key K/V tile staged in LDS serves all G heads;
-//   * K/V tiles go from HBM straight into a double-buffered LDS ring
+//   * workgroup = R x G waves: the G query heads of one KV head times R blocks
+//     of 32 query rows of one piece (R G = 8 where the piece allows: one
+//     workgroup per CU, two waves per SIMD); every 64-key K/V tile staged in
+//     LDS serves all R G waves, so the copy work per MFMA flop falls as 1 / R;
+//   * K/V tiles go from HBM straight into a ring of kStages LDS buffers
 //     (global_load_lds issued from asm and waited for with explicit vmcnt
-//     counts, so the copy of tile j + 1 overlaps the compute of tile j); the
-//     block ids of a tile are read once, by scalar loads;
+//     counts, so the copies of the next tiles overlap the compute of this
+//     one); the block ids of a tile are read once, by scalar loads;
 //   * LDS rows are unpadded (256 bytes) with the 16-byte chunks of row t
 //     XOR-swizzled by t % 16: the row-major score-operand reads and the
 //     transposing value reads are both free of bank conflicts;
@@ -30,9 +32,10 @@
 //     three steps ahead of their MFMA;
 //   * online softmax in the exp2 domain with a lazily raised reference
 //     maximum (rescale only past 2^8); causal masking only on tiles that
-//     straddle the diagonal (key position <= query position), tiles past the
-//     diagonal are never visited; keys past the visible range reuse the last
-//     visible row (finite data) and get probability 0;
+//     straddle a wave's diagonal (key position <= query position); a wave
+//     skips the tiles past its own diagonal (the workgroup stages up to the
+//     diagonal of its last row block); keys past the visible range reuse the
+//     last visible row (finite data) and get probability 0;
 //   * blockIdx % Hkv is the KV head, so the workgroups reading one head's keys
 //     share an XCD (and its L2); query blocks are issued longest-first.
 #include <math.h>
@@ -51,6 +54,11 @@ constexpr int kTileB = kBN * kRowB;      // one K or V tile in LDS (16 KB)
 constexpr int kSlots = 2 * kTileB / 1024;  // 64-lane copies per K+V tile pair (32)
 constexpr int kMaxWaves = 8;
 constexpr float kLazy = 8.f;
+#ifndef PF_STAGES
+#define PF_STAGES 2
+#endif
+constexpr int kStages = PF_STAGES;      // LDS ring of K/V tile pairs (32 KB each)
+static_assert(kStages >= 2 && kStages * 2 * kTileB <= 160 * 1024, "ring fits the LDS");
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -68,7 +76,8 @@ struct PrefillParams {
     int64_t num_blocks;
     int32_t C, pcp_rank, pcp_size, Hq, Hkv, G;
     float qk_scale;               // scale * log2(e)
-    int32_t nqb;                  // query blocks per piece
+    int32_t nqb;                  // workgroup query blocks (R x 32 rows) per piece
+    int32_t R, G_log2;            // row blocks per workgroup; log2 G
     float *out, *lse;
 };
 
@@ -100,14 +109,35 @@ __device__ __forceinline__ void dma16(gbyte *src, uint32_t lds) {
 }
 #pragma clang diagnostic pop
 
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Wait until at most n (wave-uniform, >= 0) of this wave's copies are
+// outstanding, rounded down to a listed count (waiting for more is safe).
+__device__ __forceinline__ void wait_copies_at_most(int n) {
+    if (n >= 48) vm_wait<48>();
+    else if (n >= 32) vm_wait<32>();
+    else if (n >= 24) vm_wait<24>();
+    else if (n >= 16) vm_wait<16>();
+    else if (n >= 12) vm_wait<12>();
+    else if (n >= 8) vm_wait<8>();
+    else if (n >= 4) vm_wait<4>();
+    else vm_wait<0>();
+}
+
 template <bool kPaged>
 __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t s_kv[2][2 * kTileB];  // [buf][K tile | V tile]
+    __shared__ __attribute__((aligned(16))) uint8_t s_kv[kStages][2 * kTileB];  // [buf][K tile | V tile]
 
     const int tid = threadIdx.x;
     const int nwaves = blockDim.x >> 6;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hw = wave & (p.G - 1), rb = wave >> p.G_log2;  // head in the group, row block
     const int G4 = lane >> 4, j16 = lane & 15;
 
     // ---- work item: KV head innermost (one XCD per head), longest first ----
@@ -118,18 +148,21 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
     const int npieces = 2 * p.pcp_size;
     const int piece = piece_slot == 0 ? p.pcp_rank : npieces - 1 - p.pcp_rank;
     const int c = p.C / npieces;                    // rows per piece
-    const int i0 = piece * c + qb * kBM;            // first query row (chunk index)
-    const int h = g * p.G + wave;                   // this wave's query head
+    const int i0 = piece * c + qb * kBM * p.R;      // first query row of the workgroup
+    const int i0w = i0 + kBM * rb;                  // first query row of this wave
+    const int h = g * p.G + hw;                     // this wave's query head
 
-    // keys visible to the block: causal -> [0, i0 + 32); paged shard -> [0, local_len)
-    const int32_t kend = kPaged ? p.local_len : min(i0 + kBM, p.C);
+    // keys staged for the workgroup (causal: [0, i0 + 32 R); paged shard:
+    // [0, local_len)) and keys visible to this wave's rows
+    const int32_t kend = kPaged ? p.local_len : min(i0 + kBM * p.R, p.C);
+    const int32_t kend_w = kPaged ? p.local_len : min(i0w + kBM, p.C);
     const int bs = 1 << p.bs_log2;
 
-    // ---- queries as the B operand: Q[i0 + 16 mb + j16][h][32 ks + 8 G4 .. +8] ----
+    // ---- queries as the B operand: Q[i0w + 16 mb + j16][h][32 ks + 8 G4 .. +8] ----
     u32x4_t qb_reg[2][4];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-        const int row = i0 + 16 * mb + j16;
+        const int row = i0w + 16 * mb + j16;
         gbyte *qrow = p.q + ((int64_t)row * p.Hq + h) * (kD * 2) + G4 * 16;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qb_reg[mb][ks] = load16(qrow + ks * 64);
@@ -202,13 +235,19 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
 
     constexpr int kPre = 3;
     const int ntile = kend > 0 ? (kend + kBN - 1) / kBN : 0;
-    if (ntile > 0) stage_issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): tile 0 landed (own copies)
-    __syncthreads();
+    const int ntile_w = kend_w > 0 ? (kend_w + kBN - 1) / kBN : 0;  // a prefix of the tiles
+    const int per_tile = kSlots / nwaves;  // this wave's copies per tile (nwaves divides 32)
+#pragma unroll
+    for (int j = 0; j < kStages - 1; ++j)
+        if (j < ntile) stage_issue(j * kBN, j);
     for (int32_t it = 0; it < ntile; ++it) {
+        // tile it has landed (own copies; later tiles may still be in flight) ...
+        wait_copies_at_most(min(kStages - 2, ntile - 1 - it) * per_tile);
+        __syncthreads();  // ... for every wave; the buffer of tile it - 1 is free again
+        if (it + kStages - 1 < ntile) stage_issue((it + kStages - 1) * kBN, (it + kStages - 1) % kStages);
+        if (it >= ntile_w) continue;  // past this wave's diagonal (uniform)
         const int32_t j0 = it * kBN;
-        const int buf = it & 1;
-        if (it + 1 < ntile) stage_issue(j0 + kBN, buf ^ 1);
+        const int buf = it % kStages;
         lds_u8 *tk = (lds_u8 *)(&s_kv[buf][0]);
         lds_u8 *tv = tk + kTileB;
 
@@ -267,11 +306,11 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
         // lane holds keys j0 + 16 kb + 4 G4 + e for query row i0 + 16 mb + j16.
         // Only tiles that reach past the visible keys or straddle the diagonal
         // need a mask (a uniform test).
-        const bool diag = !kPaged && (j0 + kBN - 1 > i0);  // some key may follow some row
-        if (diag || j0 + kBN > kend) {
+        const bool diag = !kPaged && (j0 + kBN - 1 > i0w);  // some key may follow some row
+        if (diag || j0 + kBN > kend_w) {
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) {
-                const int lim = min(kend, diag ? i0 + 16 * mb + j16 + 1 : kend) - j0 - 4 * G4;
+                const int lim = min(kend_w, diag ? i0w + 16 * mb + j16 + 1 : kend_w) - j0 - 4 * G4;
 #pragma unroll
                 for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
@@ -354,14 +393,11 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next tile has landed (own copies)
-        __syncthreads();                     // ... for all waves; this buffer is free again
     }
 
     // ---- finish: normalise and write rows of this piece ----
     bad = __syncthreads_or(bad);
-    const int local0 = qb * kBM;  // row within the piece
+    const int local0 = (qb * p.R + rb) * kBM;  // row within the piece
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
         float lt = l_run[mb];
@@ -465,12 +501,19 @@ extern "C" cp_status pcp_prefill_attn_causal(const cp_prefill_args *a, void *ws,
     p.Hkv = a->Hkv;
     p.G = G;
     p.qk_scale = a->scale * kLog2e;
-    p.nqb = rows / kBM;
+    // R row blocks per workgroup: eight waves where the piece's row blocks divide
+    int R = 8 / G;
+    while (R > 1 && (rows / kBM) % R != 0) R /= 2;
+    int G_log2 = 0;
+    while ((1 << G_log2) < G) ++G_log2;
+    p.R = R;
+    p.G_log2 = G_log2;
+    p.nqb = rows / (kBM * R);
     p.out = a->out;
     p.lse = a->lse;
     const int64_t blocks = (int64_t)2 * p.nqb * a->Hkv;
     if (blocks > 0x7fffffff) return fail(CP_E_UNSUPPORTED, "prefill: too many query blocks");
-    const int threads = 64 * G;
+    const int threads = 64 * G * R;
     if (a->kv_source == CP_KV_PAGED)
         hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)blocks), dim3(threads), 0, stream, p);
     else
