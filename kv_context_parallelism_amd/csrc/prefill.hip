@@ -22,14 +22,20 @@
 //     counts, so the copies of the next tiles overlap the compute of this
 //     one); the block ids of a tile are read once, by scalar loads;
 //   * LDS rows are unpadded (256 bytes) with the 16-byte chunks of row t
-//     XOR-swizzled by t % 16: the row-major score-operand reads and the
-//     transposing value reads are both free of bank conflicts;
-//   * scores S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with the wave's queries
-//     held in registers (each K read feeds both 16-row blocks, eight
-//     independent accumulation chains interleaved); the score tile is already
-//     in the A-operand layout of the value product; V is read by the
-//     transposing LDS read ds_read_b64_tr_b16; LDS operands are requested
-//     three steps ahead of their MFMA;
+//     XOR-swizzled by swz(t % 16), which swaps the two 2-bit halves of t % 16:
+//     the row-major score-operand reads (32 rows, one chunk) and the
+//     transposing value reads (4 rows, 4 chunks per 32 lanes) are both free of
+//     bank conflicts (measured; the plain t % 16 swizzle leaves the value
+//     reads with a 2-way conflict);
+//   * scores S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (M = 32 keys, N = the
+//     wave's 32 query rows, held in registers): two 32-key blocks per tile,
+//     two independent accumulation chains interleaved; the score tile is
+//     already in the A-operand layout of the value product (the key order
+//     inside each 16-key step is permuted identically on both operands);
+//     V is read by the transposing LDS read ds_read_b64_tr_b16; LDS operands
+//     are requested three steps ahead of their MFMA.  (The 32 x 32 shape
+//     does twice the work per instruction of the 16 x 16 one in 1.6 times
+//     its issue time on this chip);
 //   * online softmax in the exp2 domain with a lazily raised reference
 //     maximum (rescale only past 2^8); causal masking only on tiles that
 //     straddle a wave's diagonal (key position <= query position); a wave
@@ -55,13 +61,13 @@ constexpr int kSlots = 2 * kTileB / 1024;  // 64-lane copies per K+V tile pair (
 constexpr int kMaxWaves = 8;
 constexpr float kLazy = 8.f;
 #ifndef PF_STAGES
-#define PF_STAGES 2
+#define PF_STAGES 3
 #endif
 constexpr int kStages = PF_STAGES;      // LDS ring of K/V tile pairs (32 KB each)
 static_assert(kStages >= 2 && kStages * 2 * kTileB <= 160 * 1024, "ring fits the LDS");
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -81,10 +87,17 @@ struct PrefillParams {
     float *out, *lse;
 };
 
-__device__ __forceinline__ f32x4_t mfma16(const u32x4_t &a, const u32x4_t &b, const f32x4_t &c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+// D (32 x 32) += A (32 x 16) B (16 x 32); lane l holds A[l % 32][8 (l / 32) + e],
+// B[8 (l / 32) + e][l % 32] (e = 0 .. 7) and D[acc_row(e, l / 32)][l % 32]
+// (e = 0 .. 15).
+__device__ __forceinline__ f32x16_t mfma32(const u32x4_t &a, const u32x4_t &b, const f32x16_t &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
+__device__ __forceinline__ constexpr int acc_row(int e, int hf) { return 8 * (e >> 2) + 4 * hf + (e & 3); }
+
+// Chunk c of tile row t sits at chunk position c ^ swz(t % 16).
+__device__ __forceinline__ int swz(int t16) { return ((t16 & 3) << 2) | ((t16 >> 2) & 3); }
 
 // The lane id, recomputed where it is used: keeps per-lane addresses from
 // being hoisted out of the tile loop and held in registers.
@@ -138,7 +151,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int hw = wave & (p.G - 1), rb = wave >> p.G_log2;  // head in the group, row block
-    const int G4 = lane >> 4, j16 = lane & 15;
+    const int hf = lane >> 5, r32 = lane & 31;
 
     // ---- work item: KV head innermost (one XCD per head), longest first ----
     const int g = blockIdx.x % p.Hkv;
@@ -158,23 +171,28 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
     const int32_t kend_w = kPaged ? p.local_len : min(i0w + kBM, p.C);
     const int bs = 1 << p.bs_log2;
 
-    // ---- queries as the B operand: Q[i0w + 16 mb + j16][h][32 ks + 8 G4 .. +8] ----
-    u32x4_t qb_reg[2][4];
+    // ---- queries as the B operand: lane l holds Q[i0w + l % 32][h][16 ks + 8 (l / 32) .. +8] ----
+    u32x4_t qb_reg[8];
+    {
+        gbyte *qrow = p.q + ((int64_t)(i0w + r32) * p.Hq + h) * (kD * 2) + hf * 16;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int row = i0w + 16 * mb + j16;
-        gbyte *qrow = p.q + ((int64_t)row * p.Hq + h) * (kD * 2) + G4 * 16;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qb_reg[mb][ks] = load16(qrow + ks * 64);
+        for (int ks = 0; ks < 8; ++ks) qb_reg[ks] = load16(qrow + ks * 32);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): queries in registers before any copy
 
     // ---- tile staging: 64 key rows of K and V straight into LDS ----
     bool bad = false;
     const uint32_t kv_lds = (uint32_t)(uintptr_t)(lds_u8 *)(&s_kv[0][0]);
-    auto stage_issue = [&](int32_t j0, int buf) {
-        // base row of each 16-key group of the tile (uniform: scalar loads)
-        int64_t base[4];
+    // A tile's copy is split in two: its block ids (scalar loads, looked up
+    // before the barrier that their latency then overlaps) and its per-wave
+    // copies, which a deeper ring spreads over the wave's MFMA steps (a burst
+    // of copies from every wave fills the vector-memory queue and stalls all
+    // of them).  Copy k of this wave is slot sl = wave + k * nwaves.
+    struct TileSrc {
+        int64_t base[4];  // base row of each 16-key group of the tile
+    };
+    auto stage_rows = [&](int32_t j0) -> TileSrc {
+        TileSrc ts;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
             const int32_t t = min(j0 + 16 * q4, kend - 1);
@@ -183,99 +201,158 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
                 const bool ok = phys >= 0 && (int64_t)phys < p.num_blocks;
                 bad |= !ok;
                 phys = ok ? phys : 0;
-                base[q4] = ((int64_t)phys * p.Hkv + g) * bs + (t & (bs - 1) & ~15);
+                ts.base[q4] = ((int64_t)phys * p.Hkv + g) * bs + (t & (bs - 1) & ~15);
             } else {
-                base[q4] = (int64_t)(t & ~15) * p.Hkv + g;  // row index in units of D
+                ts.base[q4] = (int64_t)(t & ~15) * p.Hkv + g;  // row index in units of D
             }
         }
+        return ts;
+    };
+    auto stage_copy = [&](int32_t j0, int buf, const TileSrc &ts, int k) {
+        const int sl = wave + k * nwaves;
         const uint32_t dst = kv_lds + (uint32_t)(buf * 2 * kTileB);
         const int ln = lane_id_here();
         const int l16 = ln >> 4, pos = ln & 15;
+        const bool isv = sl >= kSlots / 2;
+        const int s2 = sl & (kSlots / 2 - 1);
         if (j0 + kBN <= kend) {
             // full tile: copy sl holds rows 4 (sl % 16) .. +3, all in the 16-key
             // group q4 = (sl % 16) / 4; the per-lane part of the address is
             // row r16 = 4 (sl % 4) + lane / 16 of the group and chunk
-            // (lane % 16) ^ r16 of that row
+            // (lane % 16) ^ swz(r16) of that row
             constexpr int64_t kRow = kD * 2;
             const int64_t rstride = kPaged ? kRow : (int64_t)p.Hkv * kRow;
-            for (int sl = wave; sl < kSlots; sl += nwaves) {
-                const bool isv = sl >= kSlots / 2;
-                const int s2 = sl & (kSlots / 2 - 1);
-                const int q4 = s2 >> 2;
-                const int64_t b4 = q4 == 0 ? base[0] : q4 == 1 ? base[1] : q4 == 2 ? base[2] : base[3];
-                const gbyte *gbase =
-                    (kPaged ? (isv ? p.vc : p.kc) : (isv ? p.v : p.k)) + b4 * kRow;  // uniform
-                const int r16 = 4 * (s2 & 3) + l16;
-                const uint32_t off = (uint32_t)(r16 * rstride) + (uint32_t)((pos ^ r16) * 16);
-                dma16(gbase + off, __builtin_amdgcn_readfirstlane(dst + sl * 1024));
-            }
+            const int q4 = s2 >> 2;
+            const int64_t b4 = q4 == 0 ? ts.base[0] : q4 == 1 ? ts.base[1] : q4 == 2 ? ts.base[2] : ts.base[3];
+            const gbyte *gbase = (kPaged ? (isv ? p.vc : p.kc) : (isv ? p.v : p.k)) + b4 * kRow;  // uniform
+            const int r16 = 4 * (s2 & 3) + l16;
+            const uint32_t off = (uint32_t)(r16 * rstride) + (uint32_t)((pos ^ swz(r16)) * 16);
+            dma16(gbase + off, __builtin_amdgcn_readfirstlane(dst + sl * 1024));
         } else {
-            for (int sl = wave; sl < kSlots; sl += nwaves) {
-                const bool isv = sl >= kSlots / 2;
-                const int tt = (sl & (kSlots / 2 - 1)) * 4 + l16;  // key row in the tile
-                // clamp past the visible range to the last visible key (probability 0)
-                const int tc = min(tt, kend - 1 - j0);
-                const int q4 = tc >> 4, r16 = tc & 15;
-                const int64_t b4 =
-                    q4 == 0 ? base[0] : q4 == 1 ? base[1] : q4 == 2 ? base[2] : base[3];
-                const int64_t row = kPaged ? b4 + r16 : b4 + (int64_t)r16 * p.Hkv;
-                const gbyte *src = (kPaged ? (isv ? p.vc : p.kc) : (isv ? p.v : p.k)) +
-                                   row * (kD * 2) + ((pos ^ (tt & 15)) * 16);
-                dma16(src, __builtin_amdgcn_readfirstlane(dst + sl * 1024));
-            }
+            const int tt = s2 * 4 + l16;  // key row in the tile
+            // clamp past the visible range to the last visible key (probability 0)
+            const int tc = min(tt, kend - 1 - j0);
+            const int q4 = tc >> 4, r16 = tc & 15;
+            const int64_t b4 = q4 == 0 ? ts.base[0] : q4 == 1 ? ts.base[1] : q4 == 2 ? ts.base[2] : ts.base[3];
+            const int64_t row = kPaged ? b4 + r16 : b4 + (int64_t)r16 * p.Hkv;
+            const gbyte *src = (kPaged ? (isv ? p.vc : p.kc) : (isv ? p.v : p.k)) + row * (kD * 2) +
+                               ((pos ^ swz(tt & 15)) * 16);
+            dma16(src, __builtin_amdgcn_readfirstlane(dst + sl * 1024));
         }
     };
 
-    float m_ref[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-    f32x4_t o[2][8];
+    // online-softmax state of query row i0w + l % 32 (the same in both lane halves)
+    float m_ref = -INFINITY, l_run = 0.f;
+    f32x16_t o[4];  // O[row acc_row(e, l / 32)][32 db + l % 32]
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int db = 0; db < 8; ++db) o[mb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
 
     constexpr int kPre = 3;
     const int ntile = kend > 0 ? (kend + kBN - 1) / kBN : 0;
     const int ntile_w = kend_w > 0 ? (kend_w + kBN - 1) / kBN : 0;  // a prefix of the tiles
     const int per_tile = kSlots / nwaves;  // this wave's copies per tile (nwaves divides 32)
 #pragma unroll
-    for (int j = 0; j < kStages - 1; ++j)
-        if (j < ntile) stage_issue(j * kBN, j);
+    for (int j = 0; j < kStages - 1; ++j) {
+        if (j < ntile) {
+            const TileSrc ts = stage_rows(j * kBN);
+            for (int k = 0; k < per_tile; ++k) stage_copy(j * kBN, j, ts, k);
+        }
+    }
+    // Spread copies (eight waves, full tiles, a ring of three or more): wave w
+    // copies slots w, w + 8 (K) and w + 16, w + 24 (V), i.e. key rows
+    // 16 qa + 4 (w % 4) .. +3 and 16 qb + 4 (w % 4) .. +3 of K and of V, with
+    // qa = w / 4 and qb = 2 + w / 4: two block ids and one per-lane offset.
+    const bool spread_ok = kStages >= 3 && nwaves == 8;
+    const int qa = wave >> 2, qb2 = 2 + (wave >> 2);
+    const uint32_t off8 = [&]() {
+        const int ln = lane_id_here();
+        const int r16 = 4 * (wave & 3) + (ln >> 4);
+        const int64_t rstride = kPaged ? (int64_t)kD * 2 : (int64_t)p.Hkv * kD * 2;
+        return (uint32_t)(r16 * rstride) + (uint32_t)(((ln & 15) ^ swz(r16)) * 16);
+    }();
+    auto group_row = [&](int32_t t) -> int64_t {  // base row of the 16-key group at key t
+        if constexpr (kPaged) {
+            int32_t phys = p.bt[t >> p.bs_log2];
+            const bool ok = phys >= 0 && (int64_t)phys < p.num_blocks;
+            bad |= !ok;
+            phys = ok ? phys : 0;
+            return ((int64_t)phys * p.Hkv + g) * bs + (t & (bs - 1) & ~15);
+        } else {
+            return (int64_t)(t & ~15) * p.Hkv + g;
+        }
+    };
+    const gbyte *ksrc = kPaged ? p.kc : p.k, *vsrc = kPaged ? p.vc : p.v;
     for (int32_t it = 0; it < ntile; ++it) {
+        const bool pre = it + kStages - 1 < ntile;
+        const int32_t jn = (it + kStages - 1) * kBN;
+        const int bn = (it + kStages - 1) % kStages;
+        const bool spread = spread_ok && pre && jn + kBN <= kend;
+        int64_t ra = 0, rb2 = 0;
+        if (spread) {  // scalar loads before the barrier that their latency then overlaps
+            ra = group_row(jn + 16 * qa);
+            rb2 = group_row(jn + 16 * qb2);
+        }
         // tile it has landed (own copies; later tiles may still be in flight) ...
         wait_copies_at_most(min(kStages - 2, ntile - 1 - it) * per_tile);
         __syncthreads();  // ... for every wave; the buffer of tile it - 1 is free again
-        if (it + kStages - 1 < ntile) stage_issue((it + kStages - 1) * kBN, (it + kStages - 1) % kStages);
-        if (it >= ntile_w) continue;  // past this wave's diagonal (uniform)
+        // the block ids are needed from here on: wait for them now, while no
+        // LDS read is in flight (the two share a wait counter)
+        asm volatile("" ::"s"(ra), "s"(rb2));
+        const uint32_t dstn = kv_lds + (uint32_t)(bn * 2 * kTileB) + (uint32_t)(wave * 1024);
+        // copy k of tile it + kStages - 1 goes after MFMA step 8 k + 7 of this tile
+        auto side = [&](int step) {
+            if ((step & 7) != 7 || !spread) return;
+            const int k = step >> 3;
+            const gbyte *src = ((k & 2) ? vsrc : ksrc) + ((k & 1) ? rb2 : ra) * (kD * 2);
+            dma16(src + off8, __builtin_amdgcn_readfirstlane(dstn + (uint32_t)(k * 8 * 1024)));
+        };
+        if (pre && !spread) {
+            const TileSrc ts = stage_rows(jn);
+            for (int k = 0; k < per_tile; ++k) stage_copy(jn, bn, ts, k);
+        }
+        if (it >= ntile_w) {  // past this wave's diagonal (uniform): copies only
+#pragma unroll
+            for (int st = 0; st < 32; ++st) side(st);
+            continue;
+        }
         const int32_t j0 = it * kBN;
         const int buf = it % kStages;
         lds_u8 *tk = (lds_u8 *)(&s_kv[buf][0]);
         lds_u8 *tv = tk + kTileB;
 
-        // per-lane addresses (fresh lane id per tile).  Score operand of key
-        // block kb, k-step ks: row 16 kb + j, chunk 4 ks + G; since rows
-        // 16 kb + j share the swizzle j, ks only flips the chunk bits 2..3.
-        // Value operand of column block db, key step s2: rows 32 s2 + 4 G + j / 4
-        // (and + 16), chunk 2 db + (j % 4) / 2, byte 8 (j % 2).
-        lds_u8 *ap[4], *vp[2];
+        // Per-lane addresses (fresh lane id per tile).  Score operand of key
+        // block kb, k-step ks: row 32 kb + l % 32, chunk 2 ks + l / 32 (the key
+        // block is a constant offset: rows r and r + 32 share the swizzle).
+        // Value operand of column block db, 16-key step kk: in the 16-lane group
+        // of column half g = (l / 16) % 2, lane j reads row 16 kk + 4 (l / 32) +
+        // j / 4 and the same + 8, chunk 4 db + 2 g + (j % 4) / 2, byte 8 (j % 2)
+        // (kk is a constant offset).  The swizzle mixes the lane bits into the
+        // chunk position, so each k-step and each (column block, row half) has
+        // its own lane pointer.
+        lds_u8 *ap[8], *vp[2][4];
         {
             const int ln = lane_id_here();
-            const int G = ln >> 4, j = ln & 15;
+            const int r = ln & 31, h2 = ln >> 5;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) ap[ks] = tk + j * kRowB + 16 * ((4 * ks + G) ^ j);
-            const int vr = 4 * G + (j >> 2);
-            vp[0] = tv + vr * kRowB + 8 * (j & 1);
-            vp[1] = tv + (vr + 16) * kRowB + 8 * (j & 1);
+            for (int ks = 0; ks < 8; ++ks) ap[ks] = tk + r * kRowB + 16 * ((2 * ks + h2) ^ swz(r & 15));
+            const int g = (ln >> 4) & 1, j = ln & 15;
+            const int row0 = 4 * h2 + (j >> 2), cg = 2 * g + ((j & 3) >> 1);
+#pragma unroll
+            for (int hr = 0; hr < 2; ++hr)
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+                    vp[hr][db] = tv + (row0 + 8 * hr) * kRowB + 16 * ((4 * db + cg) ^ swz(row0 + 8 * hr)) + 8 * (j & 1);
         }
-        const int vr_sw = (4 * G4 + (j16 >> 2)) & 15;  // swizzle of both value rows
-        auto read_a = [&](int i) -> u32x4_t {  // step i: ks = i / 4, kb = i % 4
-            const int ks = i >> 2, kb = i & 3;
-            return *(__attribute__((address_space(3))) const u32x4_t *)(ap[ks] + kb * 16 * kRowB);
+        auto read_a = [&](int i) -> u32x4_t {  // step i: ks = i / 2, kb = i % 2
+            const int ks = i >> 1, kb = i & 1;
+            return *(__attribute__((address_space(3))) const u32x4_t *)(ap[ks] + kb * 32 * kRowB);
         };
-        auto read_v = [&](int i) -> u32x4_t {  // step i: s2 = i / 8, db = i % 8
-            const int s2 = i >> 3, db = i & 7;
-            const int chunk = (2 * db + ((j16 & 3) >> 1)) ^ vr_sw;
-            lds_u8 *va0 = vp[0] + s2 * 32 * kRowB + chunk * 16;
-            lds_u8 *va1 = vp[1] + s2 * 32 * kRowB + chunk * 16;
+        auto read_v = [&](int i) -> u32x4_t {  // step i: kk = i / 4, db = i % 4
+            const int kk = i >> 2, db = i & 3;
+            lds_u8 *va0 = vp[0][db] + kk * 16 * kRowB;
+            lds_u8 *va1 = vp[1][db] + kk * 16 * kRowB;
             const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) i16x4_t *)(va0));
             const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -284,9 +361,9 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
             return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
         };
 
-        // ---- scores S^T[key][row]: 4 key blocks x 2 row blocks, k-step outer ----
+        // ---- scores S^T[key][row]: 2 key blocks x 8 k-steps, key blocks interleaved ----
         // (raw dot products; the scale is applied inside the exponent below)
-        f32x4_t sc[2][4];
+        f32x16_t sc[2];
         {
             u32x4_t abuf[kPre];
 #pragma unroll
@@ -295,90 +372,75 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
             for (int i = 0; i < 16; ++i) {
                 const u32x4_t a = abuf[i % kPre];
                 if (i + kPre < 16) abuf[i % kPre] = read_a(i + kPre);
-                const int ks = i >> 2, kb = i & 3;
+                const int ks = i >> 1, kb = i & 1;
+                f32x16_t zero;
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-                    sc[mb][kb] = mfma16(a, qb_reg[mb][ks],
-                                        ks == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : sc[mb][kb]);
+                for (int e = 0; e < 16; ++e) zero[e] = 0.f;
+                sc[kb] = mfma32(a, qb_reg[ks], ks == 0 ? zero : sc[kb]);
+                __builtin_amdgcn_sched_barrier(0);
+                side(i);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
-        // lane holds keys j0 + 16 kb + 4 G4 + e for query row i0 + 16 mb + j16.
+        // lane holds keys j0 + 32 kb + acc_row(e, hf) for query row i0w + l % 32.
         // Only tiles that reach past the visible keys or straddle the diagonal
         // need a mask (a uniform test).
         const bool diag = !kPaged && (j0 + kBN - 1 > i0w);  // some key may follow some row
         if (diag || j0 + kBN > kend_w) {
+            const int lim = min(kend_w, diag ? i0w + r32 + 1 : kend_w) - j0 - 4 * hf;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const int lim = min(kend_w, diag ? i0w + 16 * mb + j16 + 1 : kend_w) - j0 - 4 * G4;
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (16 * kb + e >= lim) sc[mb][kb][e] = -INFINITY;
-            }
+                for (int e = 0; e < 16; ++e)
+                    if (32 * kb + acc_row(e, 0) >= lim) sc[kb][e] = -INFINITY;
         }
-        u32x4_t pa[2][2];
-        bool need = false;
-        float mt[2];
+        float m = sc[0][0];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            float m = fmaxf(sc[mb][0][0], sc[mb][0][1]);
-            m = fmaxf(m, fmaxf(sc[mb][0][2], sc[mb][0][3]));
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int kb = 1; kb < 4; ++kb) {
-                m = fmaxf(m, fmaxf(sc[mb][kb][0], sc[mb][kb][1]));  // v_max3
-                m = fmaxf(m, fmaxf(sc[mb][kb][2], sc[mb][kb][3]));
-            }
-            m = fmaxf(m, __shfl_xor(m, 16, 64));
-            m = fmaxf(m, __shfl_xor(m, 32, 64));
-            mt[mb] = m * p.qk_scale;  // the scale is positive: max commutes with it
-            need |= mt[mb] > m_ref[mb] + kLazy;
-        }
+            for (int e = (kb == 0 ? 1 : 0); e < 16; ++e) m = fmaxf(m, sc[kb][e]);
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        const float mt = m * p.qk_scale;  // the scale is positive: max commutes with it
+        const bool need = mt > m_ref + kLazy;
         if (__any(need)) {
             // raise the reference maximum of the rows that need it and rescale
-            // their partial sums and output rows 16 mb + 4 G4 + e
+            // their partial sums and output rows acc_row(e, hf)
+            const float mn = need ? mt : m_ref;
+            const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - mn);
+            m_ref = mn;
+            l_run *= alpha;
+            float ar[16];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const float mn = mt[mb] > m_ref[mb] + kLazy ? mt[mb] : m_ref[mb];
-                const float alpha = m_ref[mb] == -INFINITY ? 0.f : fast_exp2(m_ref[mb] - mn);
-                m_ref[mb] = mn;
-                l_run[mb] *= alpha;
-                float ar[4];
+            for (int e = 0; e < 16; ++e) ar[e] = __shfl(alpha, acc_row(e, hf), 64);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) ar[e] = __shfl(alpha, G4 * 4 + e, 64);
+            for (int db = 0; db < 4; ++db)
 #pragma unroll
-                for (int db = 0; db < 8; ++db)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[mb][db][e] *= ar[e];
-            }
+                for (int e = 0; e < 16; ++e) o[db][e] *= ar[e];
         }
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            // p = 2^(s * scale - m_ref); a row with no visible key yet keeps the
-            // reference at -inf and shifts by 0
-            const float ms = m_ref[mb] == -INFINITY ? 0.f : m_ref[mb];
-            // (the denominator is summed in fp32: the LSE needs more than the
-            // bf16 precision of the weights)
+        // p = 2^(s * scale - m_ref); a row with no visible key yet keeps the
+        // reference at -inf and shifts by 0.  (The denominator is summed in
+        // fp32: the LSE needs more than the bf16 precision of the weights.)
+        u32x4_t pa[4];
+        {
+            const float ms = m_ref == -INFINITY ? 0.f : m_ref;
             float ps = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    sc[mb][kb][e] = fast_exp2(fmaf(sc[mb][kb][e], p.qk_scale, -ms));
-                    ps += sc[mb][kb][e];
+                for (int e = 0; e < 16; ++e) {
+                    sc[kb][e] = fast_exp2(fmaf(sc[kb][e], p.qk_scale, -ms));
+                    ps += sc[kb][e];
                 }
-            l_run[mb] += ps;
-            // P as A operand for 32-key steps: k = 8 G4 + e <-> key blocks (2s, 2s+1)
+            l_run += ps;
+            // P as the A operand of 16-key step kk: elements 8 (kk % 2) .. +7 of
+            // key block kk / 2, in order
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                pa[mb][s2][0] = pack_bf16x2(sc[mb][2 * s2][0], sc[mb][2 * s2][1]);
-                pa[mb][s2][1] = pack_bf16x2(sc[mb][2 * s2][2], sc[mb][2 * s2][3]);
-                pa[mb][s2][2] = pack_bf16x2(sc[mb][2 * s2 + 1][0], sc[mb][2 * s2 + 1][1]);
-                pa[mb][s2][3] = pack_bf16x2(sc[mb][2 * s2 + 1][2], sc[mb][2 * s2 + 1][3]);
-            }
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    pa[kk][i] = pack_bf16x2(sc[kk >> 1][8 * (kk & 1) + 2 * i], sc[kk >> 1][8 * (kk & 1) + 2 * i + 1]);
         }
-        // ---- values: O[row][d] += P[row][key] V[key][d] ----
+        // ---- values: O[row][d] += P[row][key] V[key][d], 4 column blocks x 4 key steps ----
         {
             u32x4_t vbuf[kPre];
 #pragma unroll
@@ -387,9 +449,10 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
             for (int i = 0; i < 16; ++i) {
                 const u32x4_t vb = vbuf[i % kPre];
                 if (i + kPre < 16) vbuf[i % kPre] = read_v(i + kPre);
-                const int s2 = i >> 3, db = i & 7;
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb) o[mb][db] = mfma16(pa[mb][s2], vb, o[mb][db]);
+                const int kk = i >> 2, db = i & 3;
+                o[db] = mfma32(pa[kk], vb, o[db]);
+                __builtin_amdgcn_sched_barrier(0);
+                side(16 + i);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -398,31 +461,20 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
     // ---- finish: normalise and write rows of this piece ----
     bad = __syncthreads_or(bad);
     const int local0 = (qb * p.R + rb) * kBM;  // row within the piece
+    const float lt = l_run + __shfl_xor(l_run, 32, 64);  // full sum of row l % 32
+    const float inv_r = bad ? NAN : (lt > 0.f ? 1.f / lt : 0.f);
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        float lt = l_run[mb];
-        lt += __shfl_xor(lt, 16, 64);
-        lt += __shfl_xor(lt, 32, 64);
-        float inv[4];
+    for (int e = 0; e < 16; ++e) {
+        const float iv = __shfl(inv_r, acc_row(e, hf), 64);
+        const int r = local0 + acc_row(e, hf);
+        float *dst = p.out + (((int64_t)piece_slot * c + r) * p.Hq + h) * kD + r32;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float le = __shfl(lt, G4 * 4 + e, 64);
-            inv[e] = bad ? NAN : (le > 0.f ? 1.f / le : 0.f);
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int r = local0 + 16 * mb + 4 * G4 + e;
-            float *dst = p.out + (((int64_t)piece_slot * c + r) * p.Hq + h) * kD;
-#pragma unroll
-            for (int db = 0; db < 8; ++db) dst[db * 16 + j16] = o[mb][db][e] * inv[e];
-        }
-        if (lane < 16) {
-            const int r = local0 + 16 * mb + lane;
-            p.lse[((int64_t)piece_slot * c + r) * p.Hq + h] =
-                bad ? NAN : (m_ref[mb] == -INFINITY || !(lt > 0.f)
-                                 ? -INFINITY
-                                 : (m_ref[mb] + fast_log2(lt)) * kLn2);
-        }
+        for (int db = 0; db < 4; ++db) dst[db * 32] = o[db][e] * iv;
+    }
+    if (lane < 32) {
+        const int r = local0 + lane;
+        p.lse[((int64_t)piece_slot * c + r) * p.Hq + h] =
+            bad ? NAN : (m_ref == -INFINITY || !(lt > 0.f) ? -INFINITY : (m_ref + fast_log2(lt)) * kLn2);
     }
 }
 
