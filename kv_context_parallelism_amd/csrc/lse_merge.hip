@@ -7,11 +7,19 @@
 // Bottleneck ...", section 3: correct_attn after the output exchange.)
 //
 // HBM-bound: every partial element is read once, every output written once.
-// One 256-thread workgroup per output row: the row's LSEs are reduced
-// (max, then sum of weights) across the block, then thread (column c, group
-// gi) accumulates float4 column c over the parts gi, gi+G, ..., and the G
-// group sums are added in LDS.  Rows are independent, so the grid is one
-// block per row and the loads of many rows are in flight at once.
+// Two kernels:
+//   * rows of up to 256 columns with up to kLaneParts parts (every merge of
+//     the decode and prefill paths): a group of S lanes (S = the float4
+//     columns, rounded up to a power of two, at most 64) owns a row; each lane
+//     reads the row's few LSEs itself (the group's lanes read the same
+//     addresses), keeps max, weights and their sum in registers, and
+//     accumulates its float4 columns over the parts -- no LDS, no barrier,
+//     and all of a lane's part loads in flight together.  A grid-stride loop
+//     over row groups keeps every wave busy;
+//   * otherwise one 256-thread workgroup per output row: the row's LSEs are
+//     reduced (max, then sum of weights) across the block, then thread
+//     (column c, group gi) accumulates float4 column c over the parts gi,
+//     gi+G, ..., and the G group sums are added in LDS.
 #include <math.h>
 
 #include "internal.hpp"
@@ -22,6 +30,109 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kCachedWeights = 2048;  // weights kept in LDS; beyond that, recomputed
+constexpr int kLaneParts = 64;        // parts per row above which the block kernel is used
+constexpr int kLaneCols = 4;          // float4 columns per lane (Dv <= 64 * 4 * 4)
+
+// Rows of the merge: parts, LSE and output base of row r (plain or segmented).
+struct RowParts {
+    const float *lp, *op;
+    int32_t n;
+};
+__device__ __forceinline__ RowParts row_parts(const MergeDesc &m, int64_t row) {
+    RowParts rp;
+    rp.lp = m.part_lse + row * m.l_row_stride;
+    rp.op = m.part_out + row * m.o_row_stride;
+    rp.n = m.n_parts;
+    if (m.seg) {  // parts of this row live at slots first .. first+count-1
+        const int64_t grp = row / m.rows_per_seg, sub = row % m.rows_per_seg;
+        const int64_t first = m.seg[2 * grp];
+        rp.n = m.seg[2 * grp + 1];
+        rp.lp = m.part_lse + first * m.l_part_stride + sub * m.l_row_stride;
+        rp.op = m.part_out + first * m.o_part_stride + sub * m.o_row_stride;
+    }
+    return rp;
+}
+
+// Lane-parallel merge: lane j of a kS-lane group owns float4 columns
+// j, j + kS, ... (kCols of them) of its row.  Two passes over the row's LSEs
+// (max; then weights, their sum and the weighted columns, eight parts per
+// step so that eight loads per column are in flight).
+template <bool kBf16Out, int kS, int kCols>
+__global__ void __launch_bounds__(kThreads) merge_lanes_kernel(MergeDesc m) {
+    constexpr int kRowsPerBlock = kThreads / kS;
+    constexpr int kBatch = 8;
+    const int lane_g = threadIdx.x % kS;
+    const int n4 = m.Dv / 4;
+    for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kS; row < m.rows;
+         row += (int64_t)gridDim.x * kRowsPerBlock) {
+        const RowParts rp = row_parts(m, row);
+        // 1. l = max_i L_i (NaN anywhere poisons the row)
+        float lmax = -INFINITY;
+        bool nan = false;
+        for (int i = 0; i < rp.n; ++i) {
+            const float L = rp.lp[(int64_t)i * m.l_part_stride];
+            nan |= (L != L);
+            lmax = fmaxf(lmax, L);
+        }
+        const bool empty = lmax == -INFINITY || nan;
+        // 2. a_i = exp(L_i - l), their sum, and sum_i a_i o_i
+        float asum = 0.f;
+        float4 acc[kCols];
+#pragma unroll
+        for (int cc = 0; cc < kCols; ++cc) acc[cc] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (!empty) {
+            for (int i0 = 0; i0 < rp.n; i0 += kBatch) {
+                float a[kBatch];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const float L = i0 + j < rp.n ? rp.lp[(int64_t)(i0 + j) * m.l_part_stride] : -INFINITY;
+                    a[j] = L == -INFINITY ? 0.f : expf(L - lmax);
+                    asum += a[j];
+                }
+#pragma unroll
+                for (int cc = 0; cc < kCols; ++cc) {
+                    const int c = lane_g + cc * kS;
+                    if (c < n4) {
+                        const float *op = rp.op + 4 * (int64_t)c + (int64_t)i0 * m.o_part_stride;
+                        float4 o[kBatch];
+#pragma unroll
+                        for (int j = 0; j < kBatch; ++j)  // an empty part's output is never read
+                            o[j] = a[j] > 0.f ? *reinterpret_cast<const float4 *>(op + (int64_t)j * m.o_part_stride)
+                                              : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                        for (int j = 0; j < kBatch; ++j) {
+                            acc[cc].x += a[j] * o[j].x;
+                            acc[cc].y += a[j] * o[j].y;
+                            acc[cc].z += a[j] * o[j].z;
+                            acc[cc].w += a[j] * o[j].w;
+                        }
+                    }
+                }
+            }
+        }
+        const float inv = nan ? NAN : (asum > 0.f ? 1.f / asum : 0.f);
+#pragma unroll
+        for (int cc = 0; cc < kCols; ++cc) {
+            const int c = lane_g + cc * kS;
+            if (c >= n4) break;
+            float4 v = acc[cc];
+            v.x *= inv;
+            v.y *= inv;
+            v.z *= inv;
+            v.w *= inv;
+            if (kBf16Out) {
+                u32x2 pk;
+                pk.x = pack_bf16x2(v.x, v.y);
+                pk.y = pack_bf16x2(v.z, v.w);
+                reinterpret_cast<u32x2 *>(m.out)[row * n4 + c] = pk;
+            } else {
+                reinterpret_cast<float4 *>(m.out)[row * n4 + c] = v;
+            }
+        }
+        if (m.lse_out && lane_g == 0)
+            m.lse_out[row] = nan ? NAN : (lmax == -INFINITY ? -INFINITY : lmax + logf(asum));
+    }
+}
 
 __device__ __forceinline__ float block_reduce(float v, bool is_max, float *s_red) {
     for (int x = 32; x >= 1; x >>= 1) {
@@ -44,15 +155,9 @@ __global__ void __launch_bounds__(kThreads) merge_rows_kernel(MergeDesc m) {
     __shared__ float4 s_acc[kThreads];
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x;
-    const float *lp = m.part_lse + row * m.l_row_stride;
-    const float *obase = m.part_out + row * m.o_row_stride;
-    if (m.seg) {  // parts of this row live at slots first .. first+count-1
-        const int64_t grp = row / m.rows_per_seg, sub = row % m.rows_per_seg;
-        const int64_t first = m.seg[2 * grp];
-        m.n_parts = m.seg[2 * grp + 1];
-        lp = m.part_lse + first * m.l_part_stride + sub * m.l_row_stride;
-        obase = m.part_out + first * m.o_part_stride + sub * m.o_row_stride;
-    }
+    const RowParts rp = row_parts(m, row);
+    const float *lp = rp.lp, *obase = rp.op;
+    m.n_parts = rp.n;
 
     // 1. l = max_i L_i (NaN anywhere poisons the row)
     float lmax = -INFINITY;
@@ -150,9 +255,49 @@ int device_cus() {
     return cached[dev];
 }
 
+template <bool kBf16Out, int kS, int kCols>
+void launch_lanes(const MergeDesc &m, hipStream_t stream) {
+    constexpr int kRowsPerBlock = kThreads / kS;
+    const int64_t need = (m.rows + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int64_t cap = (int64_t)device_cus() * 16;  // resident blocks, with margin
+    const unsigned grid = (unsigned)(need < cap ? need : cap);
+    hipLaunchKernelGGL((merge_lanes_kernel<kBf16Out, kS, kCols>), dim3(grid), dim3(kThreads), 0,
+                       stream, m);
+}
+
+// float4 columns -> (lanes per row, columns per lane).  Returns false (the
+// caller then uses the block kernel) when the rows are too wide, or too few
+// to give every CU a few waves of the lane layout.
+template <bool kBf16Out>
+bool launch_lanes_for(const MergeDesc &m, hipStream_t stream) {
+    const int n4 = m.Dv / 4;
+    int S = 1;
+    while (S < n4 && S < 64) S *= 2;
+    if (m.rows * S < (int64_t)device_cus() * 512) return false;
+    if (n4 <= 1) launch_lanes<kBf16Out, 1, 1>(m, stream);
+    else if (n4 <= 2) launch_lanes<kBf16Out, 2, 1>(m, stream);
+    else if (n4 <= 4) launch_lanes<kBf16Out, 4, 1>(m, stream);
+    else if (n4 <= 8) launch_lanes<kBf16Out, 8, 1>(m, stream);
+    else if (n4 <= 16) launch_lanes<kBf16Out, 16, 1>(m, stream);
+    else if (n4 <= 32) launch_lanes<kBf16Out, 32, 1>(m, stream);
+    else if (n4 <= 64) launch_lanes<kBf16Out, 64, 1>(m, stream);
+    else if (n4 <= 128) launch_lanes<kBf16Out, 64, 2>(m, stream);
+    else if (n4 <= 64 * kLaneCols) launch_lanes<kBf16Out, 64, kLaneCols>(m, stream);
+    else return false;
+    return true;
+}
+
 cp_status launch_merge(const MergeDesc &m, hipStream_t stream) {
     if (m.rows == 0) return CP_OK;
     if (m.rows > 0x7fffffff) return fail(CP_E_UNSUPPORTED, "merge: too many rows");
+    // Many rows of up to 64 * kLaneCols float4 columns with few parts take
+    // the lane-parallel kernel (a segment table's counts are a few per row by
+    // construction of the decode schedules).
+    if (m.seg || m.n_parts <= kLaneParts) {
+        const bool ok = m.out_dt == CP_BF16 ? launch_lanes_for<true>(m, stream)
+                                            : launch_lanes_for<false>(m, stream);
+        if (ok) return check_launch("lse merge");
+    }
     if (m.out_dt == CP_BF16)
         hipLaunchKernelGGL(merge_rows_kernel<true>, dim3((unsigned)m.rows), dim3(kThreads), 0,
                            stream, m);

@@ -146,29 +146,34 @@ def test_gqa_negative_controls():
     assert torch.isnan(o[3].cpu()).all()
 
 
-def test_lse_merge_against_oracle():
-    g = torch.Generator().manual_seed(77)
-    n, rows, Dv = 9, 1000, 128
+# (parts, rows, Dv): the lane-parallel merge (few parts, rows up to 1024 wide,
+# part counts not a multiple of its batch of 8) and the block merge (many
+# parts, or wider rows)
+@pytest.mark.parametrize("n,rows,Dv", [(9, 5000, 128), (3, 2700, 512), (1, 140000, 4), (13, 2600, 1024),
+                                       (100, 520, 128), (5, 530, 2048)])
+def test_lse_merge_against_oracle(n, rows, Dv):
+    g = torch.Generator().manual_seed(77 + n + Dv)
     po = torch.randn(n, rows, Dv, generator=g)
     pl = 5 * torch.randn(n, rows, generator=g)
-    pl[2, :100] = float("-inf")          # empty parts
-    po[2, :100] = float("nan")           # their outputs must not be read
-    pl[:, 500] = float("-inf")           # a row with every part empty
-    announce("lse merge n=9 rows=1000 Dv=128")
+    pl[n // 2, :100] = float("-inf")     # empty parts
+    po[n // 2, :100] = float("nan")      # their outputs must not be read
+    pl[:, rows - 3] = float("-inf")      # a row with every part empty
+    announce(f"lse merge n={n} rows={rows} Dv={Dv}")
     mo, ml = cp.cp_lse_merge(po.cuda(), pl.cuda())
     mb, _ = cp.cp_lse_merge(po.cuda(), pl.cuda(), out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     ro, rl = oracle.lse_merge(po.double().numpy(), pl.double().numpy())
     gate_f32(mo.cpu().numpy(), ro, "merge out")
     gate_f32(ml.cpu().numpy(), rl, "merge lse")
-    assert (mo[500] == 0).all() and torch.isneginf(ml[500])
-    ref_bf = torch.from_numpy(ro).float().to(torch.bfloat16)
-    # bf16 output: one rounding of the fp32 result (allow a one-ulp difference)
-    diff = (mb.cpu().float() - ref_bf.float()).abs()
-    assert (diff <= ref_bf.float().abs() * 2 ** -7 + 1e-30).all()
+    assert (mo[rows - 3] == 0).all() and torch.isneginf(ml[rows - 3])
+    # bf16 output: exactly the round-to-nearest-even of the same kernel's fp32
+    # result (the fp32 result is gated against the oracle above; near-zero
+    # outputs of cancelling sums keep only the fp32 gate's absolute accuracy,
+    # so a one-ulp check against the exact value would not hold there)
+    assert torch.equal(mb.cpu(), mo.cpu().to(torch.bfloat16))
     # NaN LSE propagates to its row only
     pl2 = pl.clone()
-    pl2[4, 7] = float("nan")
+    pl2[n - 1, 7] = float("nan")
     mo2, ml2 = cp.cp_lse_merge(po.cuda(), pl2.cuda())
     assert torch.isnan(mo2[7].cpu()).all() and torch.isnan(ml2[7].cpu())
     assert torch.equal(mo2[8], mo[8])
