@@ -455,9 +455,96 @@ class PrefillBench:
                 "interleave": w.I, "block_size": w.bs}
 
 
+# ---------------------------------------------------------------------------
+# KV gather: a cached prefix reassembled from its DCP shards in position order
+# ---------------------------------------------------------------------------
+
+class KvGatherBench:
+    metric_unit = "GB/s"
+
+    def __init__(self, w, dev="cuda"):
+        import numpy as np
+        import torch
+
+        import cp_inputs as ci
+        import kv_context_parallelism_amd as cp
+
+        self.w, self.cp = w, cp
+        P = w.P
+        self.k = ci.to_storage(ci.normal((P, w.Hkv, w.D), w.seed + 2, dev), w.kv_dtype)
+        self.v = ci.to_storage(ci.normal((P, w.Hkv, w.D), w.seed + 3, dev), w.kv_dtype)
+        self.seq = torch.tensor([P], dtype=torch.int32, device=dev)
+        req = torch.zeros(P, dtype=torch.int32, device=dev)
+        pos = torch.arange(P, dtype=torch.int32, device=dev)
+        self.kc, self.vc, self.bt = [], [], []
+        for r in range(w.N):
+            ll = cp.cp_local_seq_lens(self.seq, r, w.N, w.I).cpu().numpy()
+            bt, pool = ci.block_tables((ll.astype(np.int64) + w.bs - 1) // w.bs, w.seed + 100 + r,
+                                       1.25)
+            bt_d = torch.from_numpy(bt).to(dev)
+            kc = ci.nan_fill_(torch.empty(pool, w.Hkv, w.bs, w.D, dtype=self.k.dtype, device=dev),
+                              w.kv_dtype)
+            vc = ci.nan_fill_(torch.empty_like(kc), w.kv_dtype)
+            slots = cp.cp_slot_map(req, pos, bt_d, r, w.N, w.I, w.bs)
+            cp.cp_cache_write(slots, self.k, self.v, kc, vc, w.bs)
+            self.kc.append(kc)
+            self.vc.append(vc)
+            self.bt.append(bt_d)
+        self.k_out = torch.empty(1, P, w.Hkv, w.D, dtype=self.k.dtype, device=dev)
+        self.v_out = torch.empty_like(self.k_out)
+        torch.cuda.synchronize()
+        row = w.Hkv * w.D * self.k.element_size()
+        # K and V: every row read from its shard once and written once
+        self.work_step = 2 * 2 * P * row
+        self.per_launch_work = [self.work_step]
+        self.per_launch_bytes = [self.work_step]
+        self.launches_per_step = 1
+        self.dominant = [0]
+        self.kernel_name = "cp_kv_gather (K and V, whole prefix)"
+        self.dtype = w.kv_dtype
+
+    def step(self, ev=None):
+        w = self.w
+        if ev is not None:
+            ev[0][0].record()
+        self.cp.cp_kv_gather(self.kc, self.vc, self.bt, self.seq, w.N, w.I, w.bs, 0, w.P,
+                             k_out=self.k_out, v_out=self.v_out)
+        if ev is not None:
+            ev[0][1].record()
+
+    def cpu_baseline(self, budget_s=15.0):
+        """The oracle's gather (numpy over the oracle's slot map) on windows of
+        4,096 positions of the same shard caches, until the budget is spent."""
+        import oracle
+
+        import cp_inputs as ci
+
+        w = self.w
+        caches = [ci.bits(c.cpu()) for c in self.kc] + [ci.bits(c.cpu()) for c in self.vc]
+        bts = [bt.cpu().numpy() for bt in self.bt]
+        row = w.Hkv * w.D * self.k.element_size()
+        done, t0 = 0, time.perf_counter()
+        W = 4096
+        while done + W <= w.P:
+            oracle.kv_gather(caches[:w.N], bts, [w.P], w.N, w.I, w.bs, done, W)
+            oracle.kv_gather(caches[w.N:], bts, [w.P], w.N, w.I, w.bs, done, W)
+            done += W
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return 2 * 2 * done * row / dt / 1e9, f"positions 0..{done - 1} of {w.P} (K and V)"
+
+    def config(self):
+        w = self.w
+        return {"workload": w.name, "prefix_tokens": w.P, "kv_heads": w.Hkv, "head_dim": w.D,
+                "dcp_shards": w.N, "interleave": w.I, "block_size": w.bs,
+                "window": [0, w.P]}
+
+
 BENCHES = {"gqa_decode": GqaDecodeBench, "mla_decode": MlaDecodeBench,
-           "pcp_prefill": PrefillBench}
-BENCH_WORKLOADS = ["gqa_decode_bf16", "mla_decode_bf16", "mla_decode_fp8", "pcp_prefill_bf16"]
+           "pcp_prefill": PrefillBench, "kv_gather": KvGatherBench}
+BENCH_WORKLOADS = ["gqa_decode_bf16", "mla_decode_bf16", "mla_decode_fp8", "pcp_prefill_bf16",
+                   "kv_gather_bf16"]
 
 
 def main():

@@ -234,6 +234,53 @@ cp_status pcp_prefill_attn_causal(const cp_prefill_args *args, void *workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * KV gather: the inverse of the interleaved placement ([P1] section 3, "MLA
+ * path": after the all-gather, the KV of every rank is reorganised into each
+ * request's contiguous order before attention; [P1] section 2 for the
+ * ownership and local-index rules it inverts)
+ * ------------------------------------------------------------------------ */
+
+#define CP_MAX_SHARDS 16
+
+typedef struct cp_kv_gather_args {
+    int32_t N, I, bs;       /* DCP shards (1..CP_MAX_SHARDS), interleave size, block size */
+    int32_t B;              /* requests */
+    int32_t Hkv, D;         /* heads and elements of a cache row: GQA K/V (Hkv, D) or the
+                               MLA latent (Hkv = 1, D = 576) */
+    cp_dtype dt;            /* element type of the caches and the outputs */
+    const void *const *k_caches;        /* HOST array [N] of device pointers: shard r's cache
+                                           [num_blocks[r]][Hkv][bs][D] (latent: K only) */
+    const void *const *v_caches;        /* HOST array [N] of device pointers, or NULL */
+    const int32_t *const *block_tables; /* HOST array [N] of device pointers: shard r's
+                                           [B][bt_stride] physical block of local block j */
+    const int64_t *num_blocks;          /* HOST array [N]: blocks in shard r's pool */
+    int32_t bt_stride;
+    int32_t t0, W;          /* window of global positions t0 .. t0+W-1 of every request */
+    const int32_t *seq_len; /* [B] device: global length L_b of request b */
+    void *k_out;            /* [B][W][Hkv][D] device, type dt */
+    void *v_out;            /* [B][W][Hkv][D] device; NULL iff v_caches is NULL */
+} cp_kv_gather_args;
+
+/* For every request b and window row i (global position t = t0 + i):
+ *  - t < L_b: the row is copied bit for bit from the cache of the shard that
+ *    owns t, r = floor(t/I) mod N, at local index
+ *    l = floor(t/(N*I))*I + t mod I, i.e. cache slot
+ *    block_tables[r][b][floor(l/bs)]*bs + l mod bs (the slot cp_slot_map
+ *    gives t on rank r);
+ *  - t >= L_b: the row is zero;
+ *  - a local block index past bt_stride or a block id outside
+ *    [0, num_blocks[r]): the row is filled with 0xFF bytes (NaN in every
+ *    supported dtype).
+ * The output is token-major, so a window of the cached prefix can feed
+ * pcp_prefill_attn_causal's CP_KV_DENSE source.
+ * Supported: D * elem_size a multiple of 16; for Hkv > 1 also Hkv and
+ * D * elem_size / 16 powers of two.
+ * Errors: CP_E_INVALID (N outside 1..CP_MAX_SHARDS, I, bs, B, W, t0 < 0,
+ * NULL or misaligned pointers, v_out without v_caches or the reverse),
+ * CP_E_UNSUPPORTED (row shape). */
+cp_status cp_kv_gather(const cp_kv_gather_args *args, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Workspace sizing
  * ------------------------------------------------------------------------ */
 #define CP_OP_DECODE_GQA 1

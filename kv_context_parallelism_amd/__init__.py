@@ -17,12 +17,12 @@ import torch
 from . import _lib
 from ._lib import (CP_BF16, CP_E_HIP, CP_E_INVALID, CP_E_UNSUPPORTED, CP_E_WORKSPACE, CP_F32,
                    CP_FP8_E4M3FN, CP_KV_DENSE, CP_KV_PAGED, CP_OK, CP_OP_DECODE_GQA,
-                   CP_OP_DECODE_MLA, CP_OP_PREFILL, CP_SLOT_INVALID, CP_SLOT_NOT_MINE)
+                   CP_OP_DECODE_MLA, CP_OP_PREFILL, CP_SLOT_INVALID, CP_SLOT_NOT_MINE, CP_MAX_SHARDS)
 
 __all__ = [
     "CpError", "cp_local_seq_lens", "cp_slot_map", "cp_cache_write", "cp_decode_attn_partial_gqa",
     "cp_decode_attn_partial_mla", "cp_lse_merge", "pcp_prefill_attn_causal", "cp_workspace_bytes",
-    "gqa_args", "mla_args", "prefill_args", "library_path",
+    "gqa_args", "mla_args", "prefill_args", "library_path", "cp_kv_gather", "kv_gather_args",
 ]
 
 _DT = {torch.float32: CP_F32, torch.bfloat16: CP_BF16, torch.float8_e4m3fn: CP_FP8_E4M3FN}
@@ -264,3 +264,53 @@ def pcp_prefill_attn_causal(q, P, pcp_rank, pcp_size, scale, *, k=None, v=None, 
     _check(lib.pcp_prefill_attn_causal(ctypes.byref(a), None, 0, _stream(stream)),
            "pcp_prefill_attn_causal")
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# KV gather (the inverse of the interleaved placement)
+# ---------------------------------------------------------------------------
+
+def kv_gather_args(k_caches, v_caches, block_tables, seq_len, N: int, I: int, bs: int, t0: int,
+                   W: int, k_out, v_out):
+    """The argument struct plus the host pointer arrays it refers to (keep the
+    returned tuple alive for the duration of the call)."""
+    if len(k_caches) != N or len(block_tables) != N or (v_caches is not None and len(v_caches) != N):
+        raise ValueError("one cache and one block table per shard")
+    kc0 = k_caches[0]
+    Hkv, D = (kc0.shape[1], kc0.shape[3]) if kc0.dim() == 4 else (1, kc0.shape[2])
+    arr = ctypes.c_void_p * N
+    kp = arr(*[_ptr(c).value for c in k_caches])
+    vp = arr(*[_ptr(c).value for c in v_caches]) if v_caches is not None else None
+    for bt in block_tables:
+        _i32(bt, "block_table")
+    bp = arr(*[_ptr(bt).value for bt in block_tables])
+    nb = (ctypes.c_int64 * N)(*[int(c.shape[0]) for c in k_caches])
+    a = _lib.CpKvGatherArgs(N=N, I=I, bs=bs, B=int(seq_len.shape[0]), Hkv=Hkv, D=D, dt=_dt(kc0),
+                            k_caches=ctypes.cast(kp, ctypes.c_void_p),
+                            v_caches=ctypes.cast(vp, ctypes.c_void_p) if vp is not None else None,
+                            block_tables=ctypes.cast(bp, ctypes.c_void_p),
+                            num_blocks=ctypes.cast(nb, ctypes.c_void_p),
+                            bt_stride=int(block_tables[0].shape[1]), t0=t0, W=W,
+                            seq_len=_i32(seq_len, "seq_len"), k_out=_ptr(k_out), v_out=_ptr(v_out))
+    return a, (kp, vp, bp, nb)
+
+
+def cp_kv_gather(k_caches, v_caches, block_tables, seq_len, N: int, I: int, bs: int, t0: int,
+                 W: int, k_out=None, v_out=None, stream=None):
+    """Window [t0, t0 + W) of every request's KV, gathered from the N shard
+    caches (each [num_blocks][Hkv][bs][D], or [num_blocks][bs][D] for a latent
+    cache) through their block tables ([B][bt_stride] int32 each).  Returns
+    (k_out, v_out) of shape [B][W][Hkv][D] (v_out None without v_caches)."""
+    lib = _lib.load()
+    kc0 = k_caches[0]
+    Hkv, D = (kc0.shape[1], kc0.shape[3]) if kc0.dim() == 4 else (1, kc0.shape[2])
+    B = int(seq_len.shape[0])
+    if k_out is None:
+        k_out = torch.empty(B, W, Hkv, D, dtype=kc0.dtype, device=kc0.device)
+    if v_out is None and v_caches is not None:
+        v_out = torch.empty(B, W, Hkv, D, dtype=kc0.dtype, device=kc0.device)
+    a, keep = kv_gather_args(k_caches, v_caches, block_tables, seq_len, N, I, bs, t0, W, k_out,
+                             v_out)
+    _check(lib.cp_kv_gather(ctypes.byref(a), _stream(stream)), "cp_kv_gather")
+    del keep
+    return k_out, v_out

@@ -12,6 +12,7 @@ CP_F32, CP_BF16, CP_FP8_E4M3FN = range(3)
 CP_SLOT_NOT_MINE, CP_SLOT_INVALID = -1, -2
 CP_KV_DENSE, CP_KV_PAGED = 0, 1
 CP_OP_DECODE_GQA, CP_OP_DECODE_MLA, CP_OP_PREFILL = 1, 2, 3
+CP_MAX_SHARDS = 16
 
 _vp, _i32, _i64, _f32, _int = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
                                ctypes.c_int)
@@ -39,6 +40,13 @@ class CpPrefillArgs(ctypes.Structure):
                 ("num_blocks", _i64), ("out", _vp), ("lse", _vp)]
 
 
+
+class CpKvGatherArgs(ctypes.Structure):
+    _fields_ = [("N", _i32), ("I", _i32), ("bs", _i32), ("B", _i32), ("Hkv", _i32), ("D", _i32),
+                ("dt", _int), ("k_caches", _vp), ("v_caches", _vp), ("block_tables", _vp),
+                ("num_blocks", _vp), ("bt_stride", _i32), ("t0", _i32), ("W", _i32),
+                ("seq_len", _vp), ("k_out", _vp), ("v_out", _vp)]
+
 # name -> (restype, argtypes); every function the header declares
 SIGNATURES = {
     "cp_status_str": (ctypes.c_char_p, [_int]),
@@ -52,6 +60,7 @@ SIGNATURES = {
     "cp_decode_attn_partial_mla": (_int, [ctypes.POINTER(CpMlaArgs), _vp, ctypes.c_size_t, _vp]),
     "cp_lse_merge": (_int, [_i32, _i64, _i32, _vp, _vp, _vp, _int, _vp, _vp]),
     "pcp_prefill_attn_causal": (_int, [ctypes.POINTER(CpPrefillArgs), _vp, ctypes.c_size_t, _vp]),
+    "cp_kv_gather": (_int, [ctypes.POINTER(CpKvGatherArgs), _vp]),
     "cp_workspace_bytes": (ctypes.c_size_t, [_int, _vp]),
 }
 

@@ -209,3 +209,45 @@ def pcp_rank_positions(C: int, N: int, r: int, P: int = 0) -> np.ndarray:
     assert C % (2 * N) == 0
     c = C // (2 * N)
     return np.concatenate([P + p * c + np.arange(c) for p in pcp_pieces(N, r)]).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# KV gather   ([P1] section 3 "MLA path": the gathered KV of all ranks is put
+# back into each request's own order; section 2: the placement it inverts)
+# --------------------------------------------------------------------------
+
+def kv_gather(caches, block_tables, seq_lens, N: int, I: int, bs: int, t0: int, W: int):
+    """Rows t0 .. t0+W-1 of every request's KV, read back from N shard caches.
+
+    caches[r]: raw element array [nblk][Hkv][bs][D] (or [nblk][bs][D] for a
+    latent cache) of rank r; block_tables[r]: [B][stride] int32.  Row (b, i) is
+    position t = t0 + i of request b: for t < L_b it is the cache row of rank
+    owner(t) at the slot ``slot_map`` gives t on that rank (head h at
+    [slot // bs][h][slot % bs]); for t >= L_b it is zero; where the slot map
+    reports a block index past the table (-2) or the block id lies outside the
+    cache, every byte is 0xFF.  Returns [B][W][Hkv][D] of the caches' dtype.
+    """
+    caches = [np.asarray(c) for c in caches]
+    latent = caches[0].ndim == 3
+    cs = [c[:, None, :, :] if latent else c for c in caches]  # [nblk][Hkv][bs][D]
+    Hkv, D = cs[0].shape[1], cs[0].shape[3]
+    seq_lens = np.asarray(seq_lens, dtype=np.int64)
+    B = seq_lens.shape[0]
+    out = np.zeros((B, W, Hkv, D), dtype=caches[0].dtype)
+    out_bytes = out.view(np.uint8).reshape(B, W, -1)
+    for b in range(B):
+        n = int(max(0, min(W, seq_lens[b] - t0)))
+        if n == 0:
+            continue
+        pos = np.arange(t0, t0 + n, dtype=np.int32)
+        req = np.full(n, b, dtype=np.int32)
+        for r in range(N):
+            slots = slot_map(req, pos, block_tables[r], r, N, I, bs)
+            for i in np.nonzero(slots != -1)[0]:
+                s = int(slots[i])
+                blk = s // bs if s >= 0 else -1
+                if s == -2 or blk < 0 or blk >= cs[r].shape[0]:
+                    out_bytes[b, i, :] = 0xFF
+                else:
+                    out[b, i] = cs[r][blk, :, s % bs, :]
+    return out

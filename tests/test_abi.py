@@ -25,7 +25,8 @@ def _declared_functions():
 def test_header_declares_the_six_calls():
     names = _declared_functions()
     for n in ["cp_slot_map", "cp_cache_write", "cp_decode_attn_partial_gqa",
-              "cp_decode_attn_partial_mla", "cp_lse_merge", "pcp_prefill_attn_causal"]:
+              "cp_decode_attn_partial_mla", "cp_lse_merge", "pcp_prefill_attn_causal",
+              "cp_kv_gather"]:
         assert n in names
 
 
@@ -57,6 +58,7 @@ int main(void) {
   printf("cp_gqa_args sizeof %zu\n", sizeof(cp_gqa_args));
   printf("cp_mla_args sizeof %zu\n", sizeof(cp_mla_args));
   printf("cp_prefill_args sizeof %zu\n", sizeof(cp_prefill_args));
+  printf("cp_kv_gather_args sizeof %zu\n", sizeof(cp_kv_gather_args));
   %FIELDS%
   return 0;
 }
@@ -65,7 +67,8 @@ int main(void) {
 
 @pytest.mark.parametrize("cname,pytype", [("cp_gqa_args", _lib.CpGqaArgs),
                                           ("cp_mla_args", _lib.CpMlaArgs),
-                                          ("cp_prefill_args", _lib.CpPrefillArgs)])
+                                          ("cp_prefill_args", _lib.CpPrefillArgs),
+                                          ("cp_kv_gather_args", _lib.CpKvGatherArgs)])
 def test_struct_layout_matches_c(tmp_path, cname, pytype):
     fields = "\n".join(f"F({cname}, {f})" for f, _ in pytype._fields_)
     src = tmp_path / "layout.c"
@@ -136,3 +139,31 @@ def test_mla_validation_rejects_unsupported_head_counts():
     assert lib.cp_decode_attn_partial_mla(ctypes.byref(a), None, 0, None) == 2
     a.Dk, a.bs = 576, 24
     assert lib.cp_decode_attn_partial_mla(ctypes.byref(a), None, 0, None) == 2
+
+
+def test_kv_gather_validation():
+    """cp_kv_gather refuses bad shard counts, windows, pointer pairings and row
+    shapes on the host (the host pointer arrays are never dereferenced first)."""
+    lib = _lib.load()
+    arr = (ctypes.c_void_p * 2)(16, 32)
+    nb = (ctypes.c_int64 * 2)(4, 4)
+    a = _lib.CpKvGatherArgs(N=2, I=4, bs=16, B=1, Hkv=8, D=128, dt=1,
+                            k_caches=ctypes.cast(arr, ctypes.c_void_p), v_caches=None,
+                            block_tables=ctypes.cast(arr, ctypes.c_void_p),
+                            num_blocks=ctypes.cast(nb, ctypes.c_void_p), bt_stride=4, t0=0, W=64,
+                            seq_len=16, k_out=16, v_out=None)
+    for field, bad in [("N", 0), ("N", 17), ("I", 0), ("bs", 0), ("W", -1), ("t0", -5)]:
+        old = getattr(a, field)
+        setattr(a, field, bad)
+        assert lib.cp_kv_gather(ctypes.byref(a), None) == 1, field
+        setattr(a, field, old)
+    a.v_out = 16  # v_out without v_caches
+    assert lib.cp_kv_gather(ctypes.byref(a), None) == 1
+    assert b"v_caches" in lib.cp_last_error()
+    a.v_out = None
+    a.D = 100  # 200-byte rows are not whole 16-byte chunks
+    assert lib.cp_kv_gather(ctypes.byref(a), None) == 2
+    a.D, a.Hkv = 128, 6  # Hkv > 1 must be a power of two
+    assert lib.cp_kv_gather(ctypes.byref(a), None) == 2
+    a.Hkv, a.dt = 8, 9
+    assert lib.cp_kv_gather(ctypes.byref(a), None) == 1

@@ -436,3 +436,83 @@ def test_merge_identity_associativity_and_empty_parts():
     po3 = np.array([[[1.0]], [[2.0]]])
     o3, l3 = oracle.lse_merge(po3, pl3)
     assert o3[0, 0] == 1.0 and l3[0] == 1000.0
+
+
+# ---------------------------------------------------------------------------
+# KV gather ([P1] section 3 "MLA path"): the inverse of the placement
+# ---------------------------------------------------------------------------
+
+def _scatter_shards(L, N, I, bs, row_shape, dtype, rng, poison):
+    """Seeded logical KV per request, written into N shard pools (random block
+    permutations, unused blocks and slots poisoned) through oracle.slot_map."""
+    B = len(L)
+    hi = 255 if dtype == np.uint8 else 65535
+    kv = [rng.integers(0, hi, size=(int(l),) + row_shape, dtype=dtype) for l in L]
+    caches, bts = [], []
+    for r in range(N):
+        ll = oracle.local_lens(np.asarray(L), r, N, I)
+        need = (ll + bs - 1) // bs
+        stride = int(need.max()) + 2
+        nblk = int(need.sum()) + 3
+        perm = rng.permutation(nblk)
+        bt = np.full((B, stride), -7, dtype=np.int32)
+        k = 0
+        for b in range(B):
+            for j in range(need[b]):
+                bt[b, j] = perm[k]
+                k += 1
+        Hkv = row_shape[0] if len(row_shape) == 2 else 1
+        D = row_shape[-1]
+        cache = np.full((nblk, Hkv, bs, D), poison, dtype=dtype)
+        for b in range(B):
+            pos = np.arange(L[b], dtype=np.int32)
+            sl = oracle.slot_map(np.full(L[b], b, dtype=np.int32), pos, bt, r, N, I, bs)
+            for t in np.nonzero(sl >= 0)[0]:
+                cache[sl[t] // bs, :, sl[t] % bs, :] = kv[b][t].reshape(Hkv, D)
+        caches.append(cache if len(row_shape) == 2 else cache[:, 0])  # latent: [nblk][bs][D]
+        bts.append(bt)
+    return kv, caches, bts
+
+
+@pytest.mark.parametrize("N,I,bs,row_shape,dtype", [
+    (4, 4, 16, (2, 8), np.uint16),      # the pages' I=4, N=4 ownership table
+    (3, 5, 16, (2, 8), np.uint16),      # I does not divide bs
+    (8, 16, 16, (4, 4), np.uint16),     # one virtual block fills one physical block per rank
+    (2, 1, 64, (12,), np.uint8),        # latent rows (Hkv = 1, [nblk][bs][D] cache), fp8 bytes
+    (5, 32, 16, (1, 8), np.uint16),     # I > bs
+])
+def test_kv_gather_inverts_the_placement(N, I, bs, row_shape, dtype):
+    rng = np.random.default_rng(11 + N + I + bs)
+    L = [200, 37, 0, 130, 1]
+    kv, caches, bts = _scatter_shards(L, N, I, bs, row_shape, dtype, rng, poison=0xFE)
+    full = oracle.kv_gather(caches, bts, L, N, I, bs, 0, 200)
+    for b, l in enumerate(L):
+        assert np.array_equal(full[b, :l].reshape((l,) + row_shape), kv[b]), b
+        assert (full[b, l:] == 0).all()          # past the request's end: zero rows
+    # a window straddling the ends
+    win = oracle.kv_gather(caches, bts, L, N, I, bs, 33, 100)
+    for b, l in enumerate(L):
+        n = max(0, min(100, l - 33))
+        assert np.array_equal(win[b, :n].reshape((n,) + row_shape), kv[b][33:33 + n])
+        assert (win[b, n:] == 0).all()
+    # a planted mistake: reading with the wrong interleave size must not pass
+    wrong = oracle.kv_gather(caches, bts, L, N, I + 1, bs, 0, 200)
+    assert not np.array_equal(wrong, full)
+
+
+def test_kv_gather_marks_bad_block_ids():
+    rng = np.random.default_rng(5)
+    N, I, bs = 2, 4, 16
+    L = [100]
+    kv, caches, bts = _scatter_shards(L, N, I, bs, (2, 8), np.uint16, rng, poison=0)
+    bts[1][0, 1] = 10 ** 6                # rank 1's local block 1: out of the pool
+    g = oracle.kv_gather(caches, bts, L, N, I, bs, 0, 100)
+    # rank 1 owns t with floor(t/4) odd, at local index floor(t/8)*4 + t%4; its
+    # local indices 16..31 (block 1) are positions 36..39, 44..47, 52..55, 60..63
+    bad = [t for t in range(100) if (t // I) % N == 1 and 16 <= (t // 8) * 4 + t % 4 < 32]
+    assert bad == [36, 37, 38, 39, 44, 45, 46, 47, 52, 53, 54, 55, 60, 61, 62, 63]
+    for t in range(100):
+        if t in bad:
+            assert (g[0, t] == 0xFFFF).all()
+        else:
+            assert np.array_equal(g[0, t], kv[0][t])
