@@ -456,6 +456,119 @@ class PrefillBench:
 
 
 # ---------------------------------------------------------------------------
+# DCP-sharded causal prefill: the new chunk's KV interleaved like the prefix's
+# ---------------------------------------------------------------------------
+
+class DcpPrefillBench:
+    metric_unit = "TFLOP/s"
+
+    def __init__(self, w, dev="cuda"):
+        import numpy as np
+        import torch
+
+        import cp_inputs as ci
+        import kv_context_parallelism_amd as cp
+
+        self.w, self.cp = w, cp
+        C, P = w.C, w.P
+        self.q = ci.to_storage(ci.normal((C, w.Hq, w.D), w.seed + 1, dev), "bf16")
+        self.k = ci.to_storage(ci.normal((P + C, w.Hkv, w.D), w.seed + 2, dev), "bf16")
+        self.v = ci.to_storage(ci.normal((P + C, w.Hkv, w.D), w.seed + 3, dev), "bf16")
+        tot = torch.tensor([P + C], dtype=torch.int32, device=dev)
+        req_p = torch.zeros(P, dtype=torch.int32, device=dev)
+        pos_p = torch.arange(P, dtype=torch.int32, device=dev)
+        self.req_c = torch.zeros(C, dtype=torch.int32, device=dev)
+        self.pos_c = torch.arange(P, P + C, dtype=torch.int32, device=dev)
+        self.k_c, self.v_c = self.k[P:].contiguous(), self.v[P:].contiguous()
+        self.shards = []
+        for s in range(w.N):
+            ll = int(cp.cp_local_seq_lens(tot, s, w.N, w.I).cpu()[0])
+            bt, pool = ci.block_tables(np.array([(ll + w.bs - 1) // w.bs]), w.seed + 100 + s, 1.25)
+            bt_d = torch.from_numpy(bt).to(dev)
+            kc = ci.nan_fill_(torch.empty(pool, w.Hkv, w.bs, w.D, dtype=torch.bfloat16,
+                                          device=dev), "bf16")
+            vc = ci.nan_fill_(torch.empty_like(kc), "bf16")
+            slots = cp.cp_slot_map(req_p, pos_p, bt_d, s, w.N, w.I, w.bs)
+            cp.cp_cache_write(slots, self.k[:P].contiguous(), self.v[:P].contiguous(), kc, vc,
+                              w.bs)
+            self.shards.append(dict(ll=ll, bt_d=bt_d, bt_row=bt_d[0].contiguous(), kc=kc, vc=vc,
+                                    slots=torch.empty(C, dtype=torch.int64, device=dev)))
+        c = C // (2 * w.N)
+        self.part_out = torch.empty(w.N, 2 * c, w.Hq, w.D, dtype=torch.float32, device=dev)
+        self.part_lse = torch.empty(w.N, 2 * c, w.Hq, dtype=torch.float32, device=dev)
+        self.out = torch.empty(w.N, 2 * c, w.Hq, w.D, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(w.N, 2 * c, w.Hq, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        causal = C * (C + 1) // 2
+        # every (query, key) pair with key position <= query position, once
+        self.work_step = (causal + C * P) * w.Hq * 4 * w.D
+        # events bracket every shard call: per PCP rank one call per DCP shard
+        self.launches_per_step = w.N * w.N
+        self.dominant = list(range(w.N * w.N))
+        self.per_launch_work = [self.work_step / (w.N * w.N)]
+        kv_tok = w.Hkv * w.D * 2 * 2
+        self.per_launch_bytes = [sum(sh["ll"] for sh in self.shards) * kv_tok / w.N / w.N
+                                 + (2 * c) * w.Hq * w.D * (2 + 4)]
+        self.kernel_name = ("pcp_prefill_attn_causal over one DCP shard of prefix and chunk "
+                            "(causal on interleaved positions), average call")
+        self.dtype = "bf16"
+
+    def step(self, ev=None):
+        cp, w = self.cp, self.w
+        # the chunk's K/V into the DCP shards (positions P .. P+C-1), interleaved
+        for s, sh in enumerate(self.shards):
+            cp.cp_slot_map(self.req_c, self.pos_c, sh["bt_d"], s, w.N, w.I, w.bs, out=sh["slots"])
+            cp.cp_cache_write(sh["slots"], self.k_c, self.v_c, sh["kc"], sh["vc"], w.bs)
+        k = 0
+        for r in range(w.N):
+            for s, sh in enumerate(self.shards):
+                if ev is not None:
+                    ev[k][0].record()
+                cp.pcp_prefill_attn_causal(self.q, w.P, r, w.N, w.scale, k_cache=sh["kc"],
+                                           v_cache=sh["vc"], block_table=sh["bt_row"],
+                                           local_len=sh["ll"], dcp=(s, w.N, w.I),
+                                           out=self.part_out[s], lse=self.part_lse[s])
+                if ev is not None:
+                    ev[k][1].record()
+                k += 1
+            cp.cp_lse_merge(self.part_out, self.part_lse, out=self.out[r], lse_out=self.lse[r])
+
+    def cpu_baseline(self, budget_s=15.0):
+        import numpy as np
+
+        import cp_inputs as ci
+        import oracle
+
+        w = self.w
+        kall, vall = ci.bits(self.k.cpu()), ci.bits(self.v.cpu())
+        q = ci.bits(self.q.cpu())
+        rows = oracle.pcp_rank_positions(w.C, w.N, w.N - 1)
+        done, work, t0 = 0, 0, time.perf_counter()
+        for i in rows[::max(1, len(rows) // 64)]:
+            po, pl = [], []
+            for s in range(w.N):
+                o, l = oracle.attention(q[i:i + 1], kall, vall, key_begin=0, key_end=w.P + i + 1,
+                                        scale=w.scale, q_dtype="bf16", kv_dtype="bf16",
+                                        shard=(w.N, w.I, s))
+                po.append(o.reshape(-1, w.D))
+                pl.append(l.reshape(-1))
+            oracle.lse_merge(np.stack(po), np.stack(pl))
+            work += (w.P + int(i) + 1) * w.Hq * 4 * w.D
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return work / dt / 1e12, (f"{done} query rows of rank {w.N - 1} (all {w.Hq} heads, "
+                                  f"{w.N} causal shard partials + merge)")
+
+    def config(self):
+        w = self.w
+        return {"workload": w.name, "new_tokens": w.C, "prefix_tokens": w.P, "q_heads": w.Hq,
+                "kv_heads": w.Hkv, "head_dim": w.D, "pcp_size": w.N, "dcp_shards": w.N,
+                "interleave": w.I, "block_size": w.bs}
+
+
+# ---------------------------------------------------------------------------
 # KV gather: a cached prefix reassembled from its DCP shards in position order
 # ---------------------------------------------------------------------------
 
@@ -542,9 +655,10 @@ class KvGatherBench:
 
 
 BENCHES = {"gqa_decode": GqaDecodeBench, "mla_decode": MlaDecodeBench,
-           "pcp_prefill": PrefillBench, "kv_gather": KvGatherBench}
+           "pcp_prefill": PrefillBench, "dcp_prefill": DcpPrefillBench,
+           "kv_gather": KvGatherBench}
 BENCH_WORKLOADS = ["gqa_decode_bf16", "mla_decode_bf16", "mla_decode_fp8", "pcp_prefill_bf16",
-                   "kv_gather_bf16"]
+                   "dcp_prefill_bf16", "kv_gather_bf16"]
 
 
 def main():

@@ -38,7 +38,7 @@ ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                      # "gqa_decode" | "mla_decode" | "pcp_prefill" | "kv_gather"
+    kind: str                      # "gqa_decode" | "mla_decode" | "pcp_prefill" | "dcp_prefill" | "kv_gather"
     B: int = 1
     Hq: int = 1
     Hkv: int = 1
@@ -87,6 +87,11 @@ WORKLOADS = {
     "pcp_prefill_bf16": Workload("pcp_prefill_bf16", "pcp_prefill", B=1, Hq=32, Hkv=8, D=128,
                                  Dv=128, N=8, I=16, bs=16, q_dtype="bf16", kv_dtype="bf16",
                                  scale=1 / math.sqrt(128), C=32768, P=65536, seed=1005),
+    # DCP-sharded causal prefill: the prefill workload with the new chunk's KV
+    # also interleaved over the 8 DCP shards (prefix and chunk: 98,304 positions)
+    "dcp_prefill_bf16": Workload("dcp_prefill_bf16", "dcp_prefill", B=1, Hq=32, Hkv=8, D=128,
+                                 Dv=128, N=8, I=16, bs=16, q_dtype="bf16", kv_dtype="bf16",
+                                 scale=1 / math.sqrt(128), C=32768, P=65536, seed=1007),
     # KV gather: the prefill workload's 64K-token prefix, held in 8 DCP shards
     # (I 16, bs 16, 8 KV heads x 128, bf16 K and V), reassembled in position order
     "kv_gather_bf16": Workload("kv_gather_bf16", "kv_gather", B=1, Hkv=8, D=128, Dv=128, N=8,

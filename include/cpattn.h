@@ -197,6 +197,8 @@ cp_status cp_lse_merge(int32_t n_parts, int64_t rows, int32_t Dv, const float *p
 
 #define CP_KV_DENSE 0 /* new-chunk keys/values, contiguous, causal mask on positions */
 #define CP_KV_PAGED 1 /* one DCP shard of the cached prefix, all positions visible */
+#define CP_KV_PAGED_CAUSAL 2 /* one DCP shard holding prefix AND chunk keys (interleaved):
+                                 each query sees the shard's keys at positions <= its own */
 
 typedef struct cp_prefill_args {
     const void *q;          /* [C][Hq][D] bf16: the whole new chunk in position order */
@@ -216,6 +218,10 @@ typedef struct cp_prefill_args {
     int64_t num_blocks;
     float *out;             /* [2][C/(2*pcp_size)][Hq][D] fp32: head piece, then tail piece */
     float *lse;             /* [2][C/(2*pcp_size)][Hq] fp32 */
+    /* CP_KV_PAGED_CAUSAL (ignored otherwise): the shard's place in the DCP
+     * group; its local key l sits at global position
+     * floor(l/I)*dcp_size*I + dcp_rank*I + l mod I */
+    int32_t dcp_rank, dcp_size, dcp_interleave;
 } cp_prefill_args;
 
 /* The chunk is cut into 2*pcp_size equal pieces; rank r computes the query
@@ -226,10 +232,20 @@ typedef struct cp_prefill_args {
  *  - CP_KV_PAGED: keys are one DCP shard's prefix tokens (all before every
  *    chunk position, so no mask): the "Full Q + Partial KV" step of the
  *    AllGather-Q path; partials are then merged with cp_lse_merge.
+ *  - CP_KV_PAGED_CAUSAL: keys are one DCP shard's tokens of prefix and chunk
+ *    alike (the chunk's KV written interleaved like the prefix's, the DCP
+ *    long-prefill of [P1] section 5 "AllGather Q path"): the query at
+ *    position p sees the shard's keys at positions <= p, i.e. its first
+ *    cnt(p + 1) local keys, cnt(x) being the positions below x the shard owns
+ *    ([P1] section 2).  local_len bounds the keys (at least cnt(P + C));
+ *    merging the dcp_size shards' partials gives the causal attention over
+ *    prefix and chunk.
  * Supported: D = 128, Hq/Hkv in {1, 2, 4, 8}, bf16.
  * Workspace: none needed (cp_workspace_bytes returns 0).
  * Errors: CP_E_INVALID (C % (2*pcp_size), rank, sizes, pointers, a scale
- * that is not positive and finite), CP_E_UNSUPPORTED. */
+ * that is not positive and finite; for CP_KV_PAGED_CAUSAL a dcp_rank outside
+ * [0, dcp_size), dcp_interleave < 1 or local_len below cnt(P + C)),
+ * CP_E_UNSUPPORTED. */
 cp_status pcp_prefill_attn_causal(const cp_prefill_args *args, void *workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 

@@ -16,7 +16,8 @@ import torch
 
 from . import _lib
 from ._lib import (CP_BF16, CP_E_HIP, CP_E_INVALID, CP_E_UNSUPPORTED, CP_E_WORKSPACE, CP_F32,
-                   CP_FP8_E4M3FN, CP_KV_DENSE, CP_KV_PAGED, CP_OK, CP_OP_DECODE_GQA,
+                   CP_FP8_E4M3FN, CP_KV_DENSE, CP_KV_PAGED, CP_KV_PAGED_CAUSAL, CP_OK,
+                   CP_OP_DECODE_GQA,
                    CP_OP_DECODE_MLA, CP_OP_PREFILL, CP_SLOT_INVALID, CP_SLOT_NOT_MINE, CP_MAX_SHARDS)
 
 __all__ = [
@@ -229,28 +230,33 @@ def cp_lse_merge(part_out, part_lse, out=None, lse_out=None, out_dtype=torch.flo
 # ---------------------------------------------------------------------------
 
 def prefill_args(q, P, pcp_rank, pcp_size, scale, out, lse, *, k=None, v=None, k_cache=None,
-                 v_cache=None, block_table=None, local_len=0):
+                 v_cache=None, block_table=None, local_len=0, dcp=None):
+    """``dcp=(rank, size, interleave)`` selects the causal paged source (a DCP
+    shard holding prefix and chunk keys)."""
     C, Hq, D = q.shape
+    dr, ds, di = dcp if dcp is not None else (0, 1, 1)
     if k is not None:
         src, Hkv = CP_KV_DENSE, k.shape[1]
         nb, bs, stride = 0, 16, 1
     else:
-        src, Hkv = CP_KV_PAGED, k_cache.shape[1]
+        src, Hkv = (CP_KV_PAGED if dcp is None else CP_KV_PAGED_CAUSAL), k_cache.shape[1]
         nb, bs, stride = k_cache.shape[0], k_cache.shape[2], block_table.numel()
     return _lib.CpPrefillArgs(
         q=_ptr(q), C=C, P=P, pcp_rank=pcp_rank, pcp_size=pcp_size, Hq=Hq, Hkv=Hkv, D=D,
         scale=scale, kv_source=src, k=_ptr(k), v=_ptr(v), k_cache=_ptr(k_cache),
         v_cache=_ptr(v_cache), block_table=None if block_table is None else _i32(block_table, "bt"),
         local_len=int(local_len), bs=bs, bt_stride=stride, num_blocks=nb, out=_ptr(out),
-        lse=_ptr(lse))
+        lse=_ptr(lse), dcp_rank=dr, dcp_size=ds, dcp_interleave=di)
 
 
 def pcp_prefill_attn_causal(q, P, pcp_rank, pcp_size, scale, *, k=None, v=None, k_cache=None,
-                            v_cache=None, block_table=None, local_len=0, out=None, lse=None,
-                            stream=None):
+                            v_cache=None, block_table=None, local_len=0, dcp=None, out=None,
+                            lse=None, stream=None):
     """Rank ``pcp_rank``'s two pieces of the chunk q [C][Hq][D] (bf16) against
-    either the chunk's own keys (k, v: causal) or one DCP shard of the prefix
-    (k_cache, v_cache, block_table, local_len).  Returns (out fp32
+    the chunk's own keys (k, v: causal), one DCP shard of the prefix
+    (k_cache, v_cache, block_table, local_len), or -- with
+    ``dcp=(rank, size, interleave)`` -- one DCP shard holding prefix and chunk
+    keys, causal on their interleaved positions.  Returns (out fp32
     [2][C/2N][Hq][D], lse fp32 [2][C/2N][Hq])."""
     lib = _lib.load()
     C, Hq, D = q.shape
@@ -260,7 +266,7 @@ def pcp_prefill_attn_causal(q, P, pcp_rank, pcp_size, scale, *, k=None, v=None, 
     if lse is None:
         lse = torch.empty(2, c, Hq, dtype=torch.float32, device=q.device)
     a = prefill_args(q, P, pcp_rank, pcp_size, scale, out, lse, k=k, v=v, k_cache=k_cache,
-                     v_cache=v_cache, block_table=block_table, local_len=local_len)
+                     v_cache=v_cache, block_table=block_table, local_len=local_len, dcp=dcp)
     _check(lib.pcp_prefill_attn_causal(ctypes.byref(a), None, 0, _stream(stream)),
            "pcp_prefill_attn_causal")
     return out, lse

@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(_PKG, "libcpattn.so")
 CP_OK, CP_E_INVALID, CP_E_UNSUPPORTED, CP_E_WORKSPACE, CP_E_HIP = range(5)
 CP_F32, CP_BF16, CP_FP8_E4M3FN = range(3)
 CP_SLOT_NOT_MINE, CP_SLOT_INVALID = -1, -2
-CP_KV_DENSE, CP_KV_PAGED = 0, 1
+CP_KV_DENSE, CP_KV_PAGED, CP_KV_PAGED_CAUSAL = 0, 1, 2
 CP_OP_DECODE_GQA, CP_OP_DECODE_MLA, CP_OP_PREFILL = 1, 2, 3
 CP_MAX_SHARDS = 16
 
@@ -37,7 +37,8 @@ class CpPrefillArgs(ctypes.Structure):
                 ("Hq", _i32), ("Hkv", _i32), ("D", _i32), ("scale", _f32), ("kv_source", _i32),
                 ("k", _vp), ("v", _vp), ("k_cache", _vp), ("v_cache", _vp),
                 ("block_table", _vp), ("local_len", _i32), ("bs", _i32), ("bt_stride", _i32),
-                ("num_blocks", _i64), ("out", _vp), ("lse", _vp)]
+                ("num_blocks", _i64), ("out", _vp), ("lse", _vp), ("dcp_rank", _i32),
+                ("dcp_size", _i32), ("dcp_interleave", _i32)]
 
 
 

@@ -85,7 +85,21 @@ struct PrefillParams {
     int32_t nqb;                  // workgroup query blocks (R x 32 rows) per piece
     int32_t R, G_log2;            // row blocks per workgroup; log2 G
     float *out, *lse;
+    // causal paged source (a DCP shard holding prefix and chunk keys): the
+    // chunk's row i sits at position P + i; the shard is rank dcp_rank of
+    // dcp_size with interleave dcp_I
+    int32_t dcp_causal, P, dcp_rank, dcp_size, dcp_I;
 };
+
+// Positions below x owned by DCP rank s of N with interleave I ("Breaking the
+// Long-Sequence Inference Bottleneck ...", section 2: owner floor(t / I) mod N):
+// whole rounds of N I positions give I each, the partial round the overlap of
+// [0, x mod N I) with [s I, s I + I).
+__device__ __forceinline__ int32_t owned_below(int32_t x, int32_t s, int32_t N, int32_t I) {
+    const int32_t round = N * I;
+    const int32_t q = x / round, rem = x - q * round;
+    return q * I + min(max(rem - s * I, 0), I);
+}
 
 // D (32 x 32) += A (32 x 16) B (16 x 32); lane l holds A[l % 32][8 (l / 32) + e],
 // B[8 (l / 32) + e][l % 32] (e = 0 .. 7) and D[acc_row(e, l / 32)][l % 32]
@@ -167,8 +181,18 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
 
     // keys staged for the workgroup (causal: [0, i0 + 32 R); paged shard:
     // [0, local_len)) and keys visible to this wave's rows
-    const int32_t kend = kPaged ? p.local_len : min(i0 + kBM * p.R, p.C);
-    const int32_t kend_w = kPaged ? p.local_len : min(i0w + kBM, p.C);
+    // Key limits.  Dense (causal): row i sees chunk keys [0, i].  Paged prefix
+    // shard: every row sees all local_len keys.  Causal paged shard: the row at
+    // position P + i sees the shard's keys below owned_below(P + i + 1).
+    auto row_keys = [&](int32_t i) -> int32_t {  // keys visible to chunk row i (< C)
+        if (!kPaged) return i + 1;
+        if (!p.dcp_causal) return p.local_len;
+        return min(p.local_len, owned_below(p.P + i + 1, p.dcp_rank, p.dcp_size, p.dcp_I));
+    };
+    const int32_t kend = row_keys(min(i0 + kBM * p.R, p.C) - 1);  // staged for the workgroup
+    const int32_t kend_w = row_keys(min(i0w + kBM, p.C) - 1);     // this wave's last row
+    const int32_t kfirst_w = row_keys(i0w);                      // this wave's first row
+    const int32_t klim_r = row_keys(min(i0w + r32, p.C - 1));    // this lane's row
     const int bs = 1 << p.bs_log2;
 
     // ---- queries as the B operand: lane l holds Q[i0w + l % 32][h][16 ks + 8 (l / 32) .. +8] ----
@@ -385,9 +409,8 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
         // lane holds keys j0 + 32 kb + acc_row(e, hf) for query row i0w + l % 32.
         // Only tiles that reach past the visible keys or straddle the diagonal
         // need a mask (a uniform test).
-        const bool diag = !kPaged && (j0 + kBN - 1 > i0w);  // some key may follow some row
-        if (diag || j0 + kBN > kend_w) {
-            const int lim = min(kend_w, diag ? i0w + r32 + 1 : kend_w) - j0 - 4 * hf;
+        if (j0 + kBN > kfirst_w) {  // some key of the tile is past some row's limit
+            const int lim = klim_r - j0 - 4 * hf;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -513,8 +536,26 @@ extern "C" cp_status pcp_prefill_attn_causal(const cp_prefill_args *a, void *ws,
     if (rows % kBM != 0)
         return fail(CP_E_UNSUPPORTED, "prefill: piece of %d rows is not a multiple of %d", rows,
                     kBM);
-    if (a->kv_source != CP_KV_DENSE && a->kv_source != CP_KV_PAGED)
+    if (a->kv_source != CP_KV_DENSE && a->kv_source != CP_KV_PAGED &&
+        a->kv_source != CP_KV_PAGED_CAUSAL)
         return fail(CP_E_INVALID, "prefill: kv_source %d", a->kv_source);
+    const bool dcp_causal = a->kv_source == CP_KV_PAGED_CAUSAL;
+    if (dcp_causal) {
+        if (a->dcp_size < 1 || a->dcp_rank < 0 || a->dcp_rank >= a->dcp_size ||
+            a->dcp_interleave < 1 || (int64_t)a->dcp_size * a->dcp_interleave > (1 << 30) ||
+            (int64_t)a->P + a->C > 0x7ffffffe)
+            return fail(CP_E_INVALID, "prefill: dcp rank %d of %d, interleave %d, P + C = %lld",
+                        a->dcp_rank, a->dcp_size, a->dcp_interleave, (long long)a->P + a->C);
+        // the last chunk position P + C - 1 sees every shard key below P + C
+        const int64_t round = (int64_t)a->dcp_size * a->dcp_interleave, x = (int64_t)a->P + a->C;
+        const int64_t rem = x % round - (int64_t)a->dcp_rank * a->dcp_interleave;
+        const int64_t need = x / round * a->dcp_interleave +
+                             (rem < 0 ? 0 : (rem > a->dcp_interleave ? a->dcp_interleave : rem));
+        if (a->local_len < need)
+            return fail(CP_E_INVALID,
+                        "prefill: the shard holds %d keys, positions below P + C need %lld",
+                        a->local_len, (long long)need);
+    }
     if (!(a->scale > 0.f) || !(a->scale < INFINITY))
         return fail(CP_E_INVALID, "prefill: the softmax scale must be positive and finite");
     if (a->C == 0) return CP_OK;
@@ -528,7 +569,7 @@ extern "C" cp_status pcp_prefill_attn_causal(const cp_prefill_args *a, void *ws,
             return fail(CP_E_INVALID, "prefill: k/v must be 16-byte aligned");
         p.k = to_global(a->k);
         p.v = to_global(a->v);
-    } else {
+    } else {  // CP_KV_PAGED or CP_KV_PAGED_CAUSAL
         if (!a->k_cache || !a->v_cache || !a->block_table)
             return fail(CP_E_INVALID, "prefill: paged source needs caches and a block table");
         if (a->local_len < 0 || (int64_t)a->local_len > (int64_t)a->bt_stride * a->bs)
@@ -563,10 +604,15 @@ extern "C" cp_status pcp_prefill_attn_causal(const cp_prefill_args *a, void *ws,
     p.nqb = rows / (kBM * R);
     p.out = a->out;
     p.lse = a->lse;
+    p.dcp_causal = dcp_causal ? 1 : 0;
+    p.P = a->P;
+    p.dcp_rank = dcp_causal ? a->dcp_rank : 0;
+    p.dcp_size = dcp_causal ? a->dcp_size : 1;
+    p.dcp_I = dcp_causal ? a->dcp_interleave : 1;
     const int64_t blocks = (int64_t)2 * p.nqb * a->Hkv;
     if (blocks > 0x7fffffff) return fail(CP_E_UNSUPPORTED, "prefill: too many query blocks");
     const int threads = 64 * G * R;
-    if (a->kv_source == CP_KV_PAGED)
+    if (a->kv_source != CP_KV_DENSE)
         hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)blocks), dim3(threads), 0, stream, p);
     else
         hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)blocks), dim3(threads), 0, stream,

@@ -167,3 +167,23 @@ def test_kv_gather_validation():
     assert lib.cp_kv_gather(ctypes.byref(a), None) == 2
     a.Hkv, a.dt = 8, 9
     assert lib.cp_kv_gather(ctypes.byref(a), None) == 1
+
+
+def test_prefill_dcp_causal_validation():
+    """The causal paged source checks its DCP placement and that the shard
+    holds every key the chunk's last position sees, before any launch."""
+    lib = _lib.load()
+    p = _lib.CpPrefillArgs(q=16, C=128, P=100, pcp_rank=0, pcp_size=2, Hq=32, Hkv=8, D=128,
+                           scale=0.1, kv_source=2, k_cache=16, v_cache=16, block_table=16,
+                           local_len=57, bs=16, bt_stride=8, num_blocks=64, out=16, lse=16,
+                           dcp_rank=1, dcp_size=4, dcp_interleave=16)
+    # positions below P + C = 228 owned by rank 1 of 4 with I = 16: 3 rounds of
+    # 64 give 48, the partial round [192, 228) overlaps [208, 224) in 16: 64
+    assert lib.pcp_prefill_attn_causal(ctypes.byref(p), None, 0, None) == 1
+    assert b"need 64" in lib.cp_last_error()
+    for field, bad in [("dcp_rank", 4), ("dcp_rank", -1), ("dcp_size", 0), ("dcp_interleave", 0)]:
+        p.local_len = 64
+        old = getattr(p, field)
+        setattr(p, field, bad)
+        assert lib.pcp_prefill_attn_causal(ctypes.byref(p), None, 0, None) == 1, field
+        setattr(p, field, old)

@@ -130,3 +130,84 @@ def test_prefill_negative_control_and_validation():
     # a chunk not aligned to 2N is rejected
     with pytest.raises(cp.CpError, match="CP_E_INVALID"):
         cp.pcp_prefill_attn_causal(q[:250].contiguous(), P, 0, N, scale, k=k, v=v)
+
+
+def _dcp_setup(C, P, Hq, Hkv, N_dcp, I, bs, seed, check_cache=True):
+    """Chunk queries plus the logical [prefix; chunk] K/V held, all of it,
+    interleaved in N_dcp paged shards."""
+    D = 128
+    scale = 1 / math.sqrt(D)
+    q = ci.to_storage(ci.normal((C, Hq, D), seed + 1, "cuda"), "bf16")
+    wp = ci.Workload("dcp", "gqa_decode", B=1, Hq=Hq, Hkv=Hkv, D=D, Dv=D, N=N_dcp, I=I, bs=bs,
+                     q_dtype="bf16", kv_dtype="bf16", scale=scale, seed=seed + 50)
+    allkv = build_decode_case(wp, seq=[P + C], check_cache=check_cache)
+    return q, allkv, scale
+
+
+def _dcp_partials(q, allkv, P, r, N, N_dcp, I, scale):
+    outs, lses = [], []
+    for s, sh in enumerate(allkv.shards):
+        o, l = cp.pcp_prefill_attn_causal(q, P, r, N, scale, k_cache=sh["kc"], v_cache=sh["vc"],
+                                          block_table=sh["bt_dev"][0].contiguous(),
+                                          local_len=int(sh["ll"][0]), dcp=(s, N_dcp, I))
+        outs.append(o.reshape(-1, o.shape[-2], o.shape[-1]))
+        lses.append(l.reshape(-1, l.shape[-1]))
+    return torch.stack(outs), torch.stack(lses)
+
+
+@pytest.mark.parametrize("C,P,N,Hq,Hkv,N_dcp,I", [(256, 200, 2, 32, 8, 3, 16),
+                                                   (384, 0, 3, 8, 8, 4, 64),
+                                                   (512, 777, 4, 16, 8, 2, 5),
+                                                   (256, 64, 2, 8, 1, 8, 1)])
+def test_prefill_dcp_causal_shards(C, P, N, Hq, Hkv, N_dcp, I):
+    """DCP-sharded causal prefill: every shard holds prefix and chunk keys
+    interleaved; each shard's partial is the attention over its keys at
+    positions <= the query's, and their merge is causal attention over prefix
+    and chunk.  (P = 0 with I = 64: early rows see no key of shards 1..3.)"""
+    announce(f"dcp causal prefill C={C} P={P} N={N} Hq={Hq} Hkv={Hkv} N_dcp={N_dcp} I={I}")
+    q, allkv, scale = _dcp_setup(C, P, Hq, Hkv, N_dcp, I, 16, 4700 + C + P + I)
+    kall, vall = ci.bits(allkv.k.cpu()), ci.bits(allkv.v.cpu())
+    qb = ci.bits(q.cpu())
+    for r in range(N):
+        rows = oracle.pcp_rank_positions(C, N, r)
+        po, pl = _dcp_partials(q, allkv, P, r, N, N_dcp, I, scale)
+        mo, ml = cp.cp_lse_merge(po, pl)
+        torch.cuda.synchronize()
+        po, pl, mo, ml = po.cpu().numpy(), pl.cpu().numpy(), mo.cpu().numpy(), ml.cpu().numpy()
+        for s in range(N_dcp):
+            ro, rl = oracle.attention(qb[rows], kall, vall, key_begin=0, key_end=P + rows + 1,
+                                      scale=scale, q_dtype="bf16", kv_dtype="bf16",
+                                      shard=(N_dcp, I, s))
+            gate_lowp(po[s], ro, f"shard {s} r{r}", ATOL_OUT)
+            gate_lowp(pl[s], rl, f"shard lse {s} r{r}", ATOL_LSE, norm=None)
+        ro, rl = oracle.attention(qb[rows], kall, vall, key_begin=0, key_end=P + rows + 1,
+                                  scale=scale, q_dtype="bf16", kv_dtype="bf16")
+        gate_lowp(mo, ro, f"merged r{r}", ATOL_OUT)
+        gate_lowp(ml, rl, f"merged lse r{r}", ATOL_LSE, norm=None)
+
+
+def test_prefill_dcp_causal_full_workload_sampled():
+    w = ci.WORKLOADS["dcp_prefill_bf16"]
+    announce(f"{w.name}: C={w.C} P={w.P} N={w.N} sampled rows")
+    q, allkv, scale = _dcp_setup(w.C, w.P, w.Hq, w.Hkv, w.N, w.I, w.bs, w.seed, check_cache=False)
+    kall, vall = ci.bits(allkv.k.cpu()), ci.bits(allkv.v.cpu())
+    qb = ci.bits(q.cpu())
+    rng = np.random.default_rng(w.seed)
+    c = w.C // (2 * w.N)
+    heads = [0, 17, 31]
+    for r in [0, 6]:
+        rows = oracle.pcp_rank_positions(w.C, w.N, r)
+        po, pl = _dcp_partials(q, allkv, w.P, r, w.N, w.N, w.I, scale)
+        mo, ml = cp.cp_lse_merge(po, pl)
+        torch.cuda.synchronize()
+        pick = np.unique(np.concatenate([[0, c - 1, c, 2 * c - 1], rng.integers(0, 2 * c, 3)]))
+        ro, rl = oracle.attention(qb[rows[pick]], kall, vall, key_begin=0,
+                                  key_end=w.P + rows[pick] + 1, scale=scale, q_dtype="bf16",
+                                  kv_dtype="bf16", heads=heads)
+        gate_lowp(mo.cpu().numpy()[pick][:, heads], ro, f"merged r{r}", ATOL_OUT)
+        gate_lowp(ml.cpu().numpy()[pick][:, heads], rl, f"merged lse r{r}", ATOL_LSE, norm=None)
+        s = 5
+        ro, rl = oracle.attention(qb[rows[pick]], kall, vall, key_begin=0,
+                                  key_end=w.P + rows[pick] + 1, scale=scale, q_dtype="bf16",
+                                  kv_dtype="bf16", heads=heads, shard=(w.N, w.I, s))
+        gate_lowp(po[s].cpu().numpy()[pick][:, heads], ro, f"shard {s} r{r}", ATOL_OUT)

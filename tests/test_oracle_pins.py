@@ -516,3 +516,33 @@ def test_kv_gather_marks_bad_block_ids():
             assert (g[0, t] == 0xFFFF).all()
         else:
             assert np.array_equal(g[0, t], kv[0][t])
+
+
+@pytest.mark.parametrize("N,I", [(3, 5), (4, 64), (2, 1)])
+def test_merge_of_causal_shard_partials_is_causal_attention(N, I):
+    """DCP-sharded causal prefill ([P1] section 5, "AllGather Q path" with the
+    chunk's KV interleaved like the prefix's): each shard's partial over its
+    own keys at positions <= the query's, merged exactly, is the causal
+    attention over prefix and chunk -- including rows for which a shard owns
+    no visible key (empty partial, LSE -inf)."""
+    rng = np.random.default_rng(900 + N + I)
+    P, C, H, D = 37, 48, 2, 8
+    q = rng.standard_normal((C, H, D)).astype(np.float32)
+    k = rng.standard_normal((P + C, H, D)).astype(np.float32)
+    v = rng.standard_normal((P + C, H, D)).astype(np.float32)
+    rows = np.arange(C)
+    ends = P + rows + 1
+    po, pl = [], []
+    for s in range(N):
+        o, l = oracle.attention(q, k, v, key_begin=0, key_end=ends, scale=0.3, q_dtype="f32",
+                                kv_dtype="f32", shard=(N, I, s))
+        po.append(o)
+        pl.append(l)
+    if I == 64:
+        assert np.isneginf(pl[1][0]).all()   # shard 1 owns no position below P + 1 = 38
+    mo, ml = oracle.lse_merge(np.stack(po).reshape(N, C * H, D), np.stack(pl).reshape(N, C * H))
+    ro, rl = oracle.attention(q, k, v, key_begin=0, key_end=ends, scale=0.3, q_dtype="f32",
+                              kv_dtype="f32")
+    ro, rl = ro.reshape(C * H, D), rl.reshape(C * H)
+    assert np.allclose(mo, ro, rtol=1e-12, atol=1e-12)
+    assert np.allclose(ml, rl, rtol=1e-12, atol=1e-12)
