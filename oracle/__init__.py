@@ -191,6 +191,75 @@ def lse_merge(part_out, part_lse):
 
 
 # --------------------------------------------------------------------------
+# Head-scattered exchanges around the merge   ([P3] Deep Dive 6: AG+RS, AG+AR
+# and the all-to-all path)
+# --------------------------------------------------------------------------
+
+def lse_correct(part_out_i, part_lse, rank: int):
+    """AG+RS correction of rank ``rank``'s partial ([P3] Deep Dive 6): after the
+    LSE all-gather every rank knows L = log sum_i exp(L_i) per row and scales
+    its own normalised output by exp(L_rank - L); the reduce-scatter then adds
+    the corrected outputs of all ranks.  A part with L_i = -inf gets factor 0;
+    a row whose parts are all -inf gets zeros and L = -inf.
+
+    part_out_i [rows, Dv], part_lse [n, rows] -> (corrected [rows, Dv], L [rows])."""
+    po = np.asarray(part_out_i, dtype=np.float64)
+    pl = np.asarray(part_lse, dtype=np.float64)
+    n, rows = pl.shape
+    assert po.shape[0] == rows and 0 <= rank < n
+    out = np.zeros_like(po)
+    L = np.full(rows, -np.inf)
+    for r in range(rows):
+        l = pl[:, r].max()
+        if l == -np.inf:
+            continue
+        L[r] = l + np.log(sum(np.exp(x - l) for x in pl[:, r] if x != -np.inf))
+        if pl[rank, r] != -np.inf:
+            out[r] = po[r] * np.exp(pl[rank, r] - L[r])
+    return out, L
+
+
+def a2a_pack(out, lse, N: int):
+    """All-to-all send buffer of one rank ([P3] Deep Dive 6: each partial output
+    travels with its fp32 LSE in one buffer, and destination d is sent the
+    d-th of N equal head partitions).  out [B, H, Dv], lse [B, H] ->
+    [N, B, H/N, Dv + 4] float32: the Dv outputs, the LSE, three zeros."""
+    out = np.asarray(out, dtype=np.float32)
+    lse = np.asarray(lse, dtype=np.float32)
+    B, H, Dv = out.shape
+    assert lse.shape == (B, H) and H % N == 0
+    hs = H // N
+    buf = np.zeros((N, B, hs, Dv + 4), dtype=np.float32)
+    for d in range(N):
+        for b in range(B):
+            for j in range(hs):
+                buf[d, b, j, :Dv] = out[b, d * hs + j]
+                buf[d, b, j, Dv] = lse[b, d * hs + j]
+    return buf
+
+
+def all_to_all(send):
+    """The exchange itself, on stacked per-rank send buffers: rank d receives,
+    in source order, what every rank s put in its slot d.
+    send [N_src, N_dst, ...] -> recv [N_dst, N_src, ...]."""
+    send = np.asarray(send)
+    return np.ascontiguousarray(np.swapaxes(send, 0, 1))
+
+
+def lse_merge_packed(recv, Dv: int):
+    """Exact merge of packed partials ([P3] Deep Dive 6, the LSE-weighted
+    reduction after the all-to-all): recv [n, ..., Dv + 4] holds each part's
+    outputs followed by its LSE.  Returns (out [..., Dv], lse [...])."""
+    recv = np.asarray(recv)
+    n = recv.shape[0]
+    lead = recv.shape[1:-1]
+    rows = int(np.prod(lead)) if lead else 1
+    flat = recv.reshape(n, rows, recv.shape[-1])
+    o, l = lse_merge(flat[:, :, :Dv], flat[:, :, Dv])
+    return o.reshape(*lead, Dv), l.reshape(lead)
+
+
+# --------------------------------------------------------------------------
 # PCP head-tail split   ([P1] section 4; [P3] Deep Dive 3)
 # --------------------------------------------------------------------------
 

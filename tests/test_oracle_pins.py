@@ -546,3 +546,88 @@ def test_merge_of_causal_shard_partials_is_causal_attention(N, I):
     ro, rl = ro.reshape(C * H, D), rl.reshape(C * H)
     assert np.allclose(mo, ro, rtol=1e-12, atol=1e-12)
     assert np.allclose(ml, rl, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Head-scattered exchanges ([P3] Deep Dive 6: AG+RS, and the all-to-all path)
+# ---------------------------------------------------------------------------
+
+def _shard_partials(rng, n, B, Hq, Hkv, D, N, I, scale):
+    """Every DCP shard's partial over its own keys, and torch fp64 SDPA over all
+    keys: B query rows (one per decode request, sharing one context here)."""
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    k = (3 * rng.standard_normal((n, Hkv, D))).astype(np.float32)
+    v = rng.standard_normal((n, Hkv, D)).astype(np.float32)
+    parts = [oracle.attention(q, k, v, key_begin=0, key_end=n, scale=scale, q_dtype="f32",
+                              kv_dtype="f32", shard=(N, I, r)) for r in range(N)]
+    tq = torch.from_numpy(q).double().permute(1, 0, 2)
+    tk = torch.from_numpy(k).double().permute(1, 0, 2)
+    tv = torch.from_numpy(v).double().permute(1, 0, 2)
+    ro, rl = _sdpa(tq, tk, tv, scale)
+    return parts, ro.permute(1, 0, 2).numpy(), rl.permute(1, 0).numpy()
+
+
+@pytest.mark.parametrize("N,I,n", [(4, 4, 150), (8, 16, 300), (4, 4, 5), (3, 1, 2)])
+def test_ag_rs_corrected_partials_sum_to_unsharded_attention(N, I, n):
+    """AG+RS: after the LSE all-gather each rank scales its own output by
+    exp(L_i - L); adding the N corrected outputs (what the reduce-scatter does,
+    head slice by head slice) gives exact attention over all keys.  With n = 5
+    (N = 4, I = 4) or n = 2 (N = 3) some shards own no key: LSE -inf, factor 0."""
+    rng = np.random.default_rng(1200 + N + n)
+    B, Hq, Hkv, D = 3, 8, 2, 16
+    parts, ro, rl = _shard_partials(rng, n, B, Hq, Hkv, D, N, I, 0.25)
+    pl = np.stack([p[1].reshape(B * Hq) for p in parts])
+    if n < N * I:
+        assert np.isneginf(pl[-1]).all()
+    total = np.zeros((B * Hq, D))
+    for r in range(N):
+        po_r = parts[r][0].reshape(B * Hq, D).copy()
+        if np.isneginf(pl[r]).all():
+            po_r[:] = np.nan     # an empty partial's output is never read
+        c, L = oracle.lse_correct(po_r, pl, r)
+        np.testing.assert_allclose(L, rl.reshape(-1), rtol=1e-12)
+        total += c
+    np.testing.assert_allclose(total, ro.reshape(B * Hq, D), rtol=1e-11, atol=1e-13)
+    # rank 0 alone is not the answer (the factors matter)
+    assert np.abs(parts[0][0].reshape(B * Hq, D) - ro.reshape(B * Hq, D)).max() > 1e-3
+
+
+def test_ag_rs_correction_special_rows():
+    pl = np.array([[0.0, -np.inf, np.log(3.0)], [np.log(3.0), -np.inf, -np.inf]])
+    po = np.array([[2.0, 4.0], [5.0, 6.0], [1.0, -1.0]])
+    c, L = oracle.lse_correct(po, pl, 0)
+    # row 0: L = log(1 + 3), factor 1/4; row 1: every part empty; row 2: the
+    # other part is empty, factor 1
+    np.testing.assert_allclose(L, [np.log(4.0), -np.inf, np.log(3.0)])
+    np.testing.assert_allclose(c, [[0.5, 1.0], [0.0, 0.0], [1.0, -1.0]])
+
+
+@pytest.mark.parametrize("N,Hq,Hkv", [(4, 8, 2), (2, 8, 8), (8, 16, 1)])
+def test_a2a_pack_exchange_merge_gives_head_slices(N, Hq, Hkv):
+    """All-to-all path: every rank packs its partial (outputs + fp32 LSE per
+    row) by destination head partition; after the exchange rank d merges the N
+    packed parts it received into heads d*H/N .. (d+1)*H/N - 1 of the exact
+    attention over all keys."""
+    rng = np.random.default_rng(1300 + N + Hq)
+    B, D, n = 3, 16, 90
+    parts, ro, rl = _shard_partials(rng, n, B, Hq, Hkv, D, N, 4, 0.25)
+    send = np.stack([oracle.a2a_pack(p[0].reshape(B, Hq, D), p[1].reshape(B, Hq), N)
+                     for p in parts])
+    hs = Hq // N
+    assert send.shape == (N, N, B, hs, D + 4) and send.dtype == np.float32
+    # layout: part s's slot d holds heads d*hs.., LSE in float32, three zeros
+    s, d = N - 1, N // 2
+    np.testing.assert_array_equal(send[s, d, :, :, :D],
+                                  parts[s][0].reshape(B, Hq, D)[:, d * hs:(d + 1) * hs]
+                                  .astype(np.float32))
+    np.testing.assert_array_equal(send[s, d, :, :, D],
+                                  parts[s][1].reshape(B, Hq)[:, d * hs:(d + 1) * hs]
+                                  .astype(np.float32))
+    assert (send[..., D + 1:] == 0).all()
+    recv = oracle.all_to_all(send)
+    assert np.array_equal(recv[d, s], send[s, d])
+    got = np.concatenate([oracle.lse_merge_packed(recv[d], D)[0] for d in range(N)], axis=1)
+    # float32 partials and LSEs on the wire: agreement to float32 rounding
+    np.testing.assert_allclose(got, ro, rtol=2e-5, atol=2e-6)
+    lse = np.concatenate([oracle.lse_merge_packed(recv[d], D)[1] for d in range(N)], axis=1)
+    np.testing.assert_allclose(lse, rl, rtol=1e-6, atol=1e-6)
