@@ -654,11 +654,115 @@ class KvGatherBench:
                 "window": [0, w.P]}
 
 
+# ---------------------------------------------------------------------------
+# Head-scattered output exchanges: the per-rank kernels of AG+RS and all-to-all
+# ---------------------------------------------------------------------------
+
+class HeadScatterBench:
+    """One rank's share of both exchange paths at the MLA decode shape, for
+    every layer of a decode step: the AG+RS correction of its [B][H][Dv]
+    partial (given all N ranks' LSEs), the all-to-all packing of the same
+    partial, and the exact merge of the N packed partials of its H/N-head slice
+    into the bf16 output.  Each layer has its own buffers (over 1 GB in all, so
+    that nothing is served from the last-level cache between layers); each
+    kernel runs for all layers back to back between one pair of events."""
+    metric_unit = "GB/s"
+    layers = 16
+
+    def __init__(self, w, dev="cuda"):
+        import torch
+
+        import cp_inputs as ci
+        import kv_context_parallelism_amd as cp
+
+        self.w, self.cp = w, cp
+        B, H, Dv, N = w.B, w.Hq, w.Dv, w.N
+        hs = H // N
+        self.o, self.l, self.recv = [], [], []
+        for j in range(self.layers):
+            o = ci.normal((N, B, H, Dv), w.seed + 10 * j + 1, dev)
+            l = 4 * ci.normal((N, B, H), w.seed + 10 * j + 2, dev)
+            # what rank 0 receives: slot 0 of every rank's send buffer
+            self.recv.append(torch.stack([cp.cp_a2a_pack(o[r], l[r], N)[0] for r in range(N)]))
+            self.o.append(o[0].clone())
+            self.l.append(l)
+            del o
+        self.buf = [torch.empty(N, B, hs, Dv + 4, device=dev) for _ in range(self.layers)]
+        self.corr = [torch.empty(B, H, Dv, device=dev) for _ in range(self.layers)]
+        self.L = [torch.empty(B, H, device=dev) for _ in range(self.layers)]
+        self.out = [torch.empty(B, hs, Dv, dtype=torch.bfloat16, device=dev)
+                    for _ in range(self.layers)]
+        self.lse = [torch.empty(B, hs, device=dev) for _ in range(self.layers)]
+        torch.cuda.synchronize()
+        rows = B * H
+        # algorithmic bytes: each element read once, written once (the pack
+        # writes the padding of its packed rows; the merge does not read it)
+        self.work_correct = rows * (Dv * 4 + N * 4) + rows * (Dv + 1) * 4
+        self.work_pack = rows * (Dv + 1) * 4 + rows * (Dv + 4) * 4
+        self.work_merge = (rows // N) * (N * (Dv + 1) * 4 + Dv * 2 + 4)
+        self.work_step = self.layers * (self.work_correct + self.work_pack + self.work_merge)
+        self.per_launch_work = [self.work_pack]
+        self.per_launch_bytes = [self.work_pack]
+        self.launches_per_step = 3
+        self.launches_per_event = self.layers
+        self.dominant = [1]
+        self.kernel_name = "cp_a2a_pack (one rank's partial, 8 head partitions)"
+        self.secondaries = [("cp_lse_correct (AG+RS, one rank's partial)", [0], self.work_correct),
+                            ("cp_lse_merge_packed (8 parts of a 16-head slice, bf16 out)", [2],
+                             self.work_merge)]
+        self.dtype = "f32"
+
+    def step(self, ev=None):
+        cp, N, Dv = self.cp, self.w.N, self.w.Dv
+        for k in range(3):
+            if ev is not None:
+                ev[k][0].record()
+            for j in range(self.layers):
+                if k == 0:
+                    cp.cp_lse_correct(self.o[j], self.l[j], 0, corrected=self.corr[j],
+                                      lse_out=self.L[j])
+                elif k == 1:
+                    cp.cp_a2a_pack(self.o[j], self.l[j][0], N, buf=self.buf[j])
+                else:
+                    cp.cp_lse_merge_packed(self.recv[j], Dv, out=self.out[j], lse_out=self.lse[j])
+            if ev is not None:
+                ev[k][1].record()
+
+    def cpu_baseline(self, budget_s=15.0):
+        """The oracle's correction, packing and packed merge of layer 0's
+        partials, over blocks of requests until the budget is spent."""
+        import oracle
+
+        w = self.w
+        o = self.o[0].cpu().numpy()
+        l = self.l[0].cpu().numpy()
+        recv = self.recv[0].cpu().numpy()
+        per_req = self.work_step / self.layers / w.B
+        done, t0 = 0, time.perf_counter()
+        blk = 4
+        while done + blk <= w.B:
+            sl = slice(done, done + blk)
+            oracle.lse_correct(o[sl].reshape(-1, w.Dv), l[:, sl].reshape(w.N, -1), 0)
+            oracle.a2a_pack(o[sl], l[0, sl], w.N)
+            oracle.lse_merge_packed(recv[:, sl], w.Dv)
+            done += blk
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return done * per_req / dt / 1e9, f"requests 0..{done - 1} of {w.B} of one layer, all three steps"
+
+    def config(self):
+        w = self.w
+        return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "value_dim": w.Dv,
+                "cp_ranks": w.N, "heads_per_rank": w.Hq // w.N, "layers": self.layers,
+                "partials": "fp32 out + fp32 LSE", "merged_out": "bf16"}
+
+
 BENCHES = {"gqa_decode": GqaDecodeBench, "mla_decode": MlaDecodeBench,
            "pcp_prefill": PrefillBench, "dcp_prefill": DcpPrefillBench,
-           "kv_gather": KvGatherBench}
+           "kv_gather": KvGatherBench, "head_scatter": HeadScatterBench}
 BENCH_WORKLOADS = ["gqa_decode_bf16", "mla_decode_bf16", "mla_decode_fp8", "pcp_prefill_bf16",
-                   "dcp_prefill_bf16", "kv_gather_bf16"]
+                   "dcp_prefill_bf16", "kv_gather_bf16", "head_scatter_mla"]
 
 
 def main():
@@ -710,7 +814,8 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
     launch_ms = [step[k][0].elapsed_time(step[k][1]) for step in ev for k in bench.dominant]
-    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    per_event = getattr(bench, "launches_per_event", 1)  # launches between one event pair
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3 / per_event
     unit = bench.metric_unit
     if unit == "GB/s":
         scale_v, peak, bound = 1e9, HBM_PEAK_GBS, "hbm"
@@ -735,6 +840,14 @@ def main():
                              "avg_launch_us": round(sec_s * 1e6, 2),
                              "achieved": round(bench.secondary_work / sec_s / scale_v, 2),
                              "frac": round(bench.secondary_work / sec_s / scale_v / peak, 4)}
+    if getattr(bench, "secondaries", None):
+        roof["secondary"] = []
+        for name, idx, work in bench.secondaries:
+            sec_ms = [step[k][0].elapsed_time(step[k][1]) for step in ev for k in idx]
+            sec_s = sum(sec_ms) / len(sec_ms) / 1e3 / per_event
+            roof["secondary"].append({"kernel": name, "avg_launch_us": round(sec_s * 1e6, 2),
+                                      "achieved": round(work / sec_s / scale_v, 2),
+                                      "frac": round(work / sec_s / scale_v / peak, 4)})
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),

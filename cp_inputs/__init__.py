@@ -38,7 +38,8 @@ ELEM_BYTES = {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str                      # "gqa_decode" | "mla_decode" | "pcp_prefill" | "dcp_prefill" | "kv_gather"
+    kind: str                      # "gqa_decode" | "mla_decode" | "pcp_prefill" | "dcp_prefill"
+                                   # | "kv_gather" | "head_scatter"
     B: int = 1
     Hq: int = 1
     Hkv: int = 1
@@ -96,6 +97,11 @@ WORKLOADS = {
     # (I 16, bs 16, 8 KV heads x 128, bf16 K and V), reassembled in position order
     "kv_gather_bf16": Workload("kv_gather_bf16", "kv_gather", B=1, Hkv=8, D=128, Dv=128, N=8,
                                I=16, bs=16, kv_dtype="bf16", P=65536, seed=1006),
+    # Head-scattered output exchanges at the MLA decode shape: one rank's
+    # partials for 64 requests x 128 heads x 512 (fp32 outputs and LSEs) and
+    # the 8 packed partials of its 16-head slice that the all-to-all delivers
+    "head_scatter_mla": Workload("head_scatter_mla", "head_scatter", B=64, Hq=128, Dv=512, N=8,
+                                 seed=1008),
 }
 
 

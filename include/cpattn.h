@@ -190,6 +190,47 @@ cp_status cp_lse_merge(int32_t n_parts, int64_t rows, int32_t Dv, const float *p
                        hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Head-scattered exchange steps around the merge ([P3] Deep Dive 6: the
+ * AG+RS path corrects every rank's output after the LSE all-gather and
+ * reduce-scatters heads; the A2A path packs each partial output with its fp32
+ * LSE into one buffer, exchanges head partitions with one all-to-all and
+ * reduces them exactly).  The collectives themselves are not part of this
+ * library; these are the per-rank kernels on either side of them.
+ * ------------------------------------------------------------------------ */
+
+/* AG+RS correction of one rank's partial: with L = log sum_i exp(L_i) over
+ * the n_parts gathered LSEs of each row,
+ *     corrected[r][d] = part_out_i[r][d] * exp(L_i[r] - L[r]),
+ * so that summing the n_parts corrected outputs (the reduce-scatter) gives the
+ * merged output.  part_out_i [rows][Dv] is rank `rank`'s partial, part_lse
+ * [n_parts][rows] every rank's LSE.  lse_out [rows] (may be NULL) receives L.
+ * A part with L_i = -inf gets factor 0 (its output is not read); a row whose
+ * parts are all -inf gets zeros and L = -inf; a NaN LSE gives a NaN row.
+ * Errors: as cp_lse_merge, plus CP_E_INVALID for rank outside [0, n_parts). */
+cp_status cp_lse_correct(int32_t n_parts, int64_t rows, int32_t Dv, int32_t rank,
+                         const float *part_out_i, const float *part_lse, float *corrected,
+                         float *lse_out, hipStream_t stream);
+
+/* A2A packing of one rank's partial: out [B][H][Dv] and lse [B][H] (fp32) go
+ * to buf [N][B][H/N][Dv + 4] fp32, destination d getting heads
+ * d*H/N .. (d+1)*H/N - 1; a packed row is the Dv outputs, the LSE, and three
+ * zero floats (rows stay 16-byte aligned).  Requires H % N == 0, Dv % 4 == 0.
+ * Errors: CP_E_INVALID (sizes, H % N, NULL or misaligned pointers),
+ * CP_E_UNSUPPORTED (Dv % 4). */
+cp_status cp_a2a_pack(int32_t B, int32_t H, int32_t Dv, int32_t N, const float *out,
+                      const float *lse, float *buf, hipStream_t stream);
+
+/* Exact merge of n_parts packed partials (after the all-to-all): part i of
+ * row r is at packed[i * part_stride + r * (Dv + 4)] (Dv outputs, then the
+ * LSE), part_stride >= rows * (Dv + 4) floats.  Same arithmetic and output
+ * contract as cp_lse_merge.
+ * Errors: as cp_lse_merge, plus CP_E_INVALID for a part_stride below
+ * rows * (Dv + 4). */
+cp_status cp_lse_merge_packed(int32_t n_parts, int64_t rows, int32_t Dv, const float *packed,
+                              int64_t part_stride, void *out, cp_dtype out_dt, float *lse_out,
+                              hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * PCP load-balanced causal prefill ([P1] section 4 "Head-tail concatenation
  * strategy" and "Minimal state progression"; section 5 "AllGather Q path";
  * [P3] Deep Dive 3)

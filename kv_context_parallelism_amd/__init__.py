@@ -22,7 +22,8 @@ from ._lib import (CP_BF16, CP_E_HIP, CP_E_INVALID, CP_E_UNSUPPORTED, CP_E_WORKS
 
 __all__ = [
     "CpError", "cp_local_seq_lens", "cp_slot_map", "cp_cache_write", "cp_decode_attn_partial_gqa",
-    "cp_decode_attn_partial_mla", "cp_lse_merge", "pcp_prefill_attn_causal", "cp_workspace_bytes",
+    "cp_decode_attn_partial_mla", "cp_lse_merge", "cp_lse_correct", "cp_a2a_pack",
+    "cp_lse_merge_packed", "pcp_prefill_attn_causal", "cp_workspace_bytes",
     "gqa_args", "mla_args", "prefill_args", "library_path", "cp_kv_gather", "kv_gather_args",
 ]
 
@@ -222,6 +223,68 @@ def cp_lse_merge(part_out, part_lse, out=None, lse_out=None, out_dtype=torch.flo
         lse_out = torch.empty(part_lse.shape[1:], dtype=torch.float32, device=part_out.device)
     _check(lib.cp_lse_merge(n, rows, Dv, _ptr(part_out), _ptr(part_lse), _ptr(out), _dt(out),
                             _ptr(lse_out), _stream(stream)), "cp_lse_merge")
+    return out, lse_out
+
+
+def cp_lse_correct(part_out_i, part_lse, rank, corrected=None, lse_out=None, stream=None):
+    """AG+RS correction of one rank's partial part_out_i [rows...][Dv] given
+    every rank's LSE part_lse [n][rows...]: part_out_i * exp(L_rank - L)."""
+    lib = _lib.load()
+    n = part_lse.shape[0]
+    Dv = part_out_i.shape[-1]
+    rows = part_lse[0].numel()
+    if part_out_i.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise ValueError("partials must be fp32")
+    if part_out_i.numel() != rows * Dv:
+        raise ValueError("part_out_i / part_lse shape mismatch")
+    if corrected is None:
+        corrected = torch.empty_like(part_out_i)
+    if lse_out is None:
+        lse_out = torch.empty(part_lse.shape[1:], dtype=torch.float32, device=part_lse.device)
+    _check(lib.cp_lse_correct(n, rows, Dv, int(rank), _ptr(part_out_i), _ptr(part_lse),
+                              _ptr(corrected), _ptr(lse_out), _stream(stream)), "cp_lse_correct")
+    return corrected, lse_out
+
+
+def cp_a2a_pack(out, lse, N, buf=None, stream=None):
+    """All-to-all send buffer [N][B][H/N][Dv+4] of one rank's out [B][H][Dv]
+    and lse [B][H] (fp32)."""
+    lib = _lib.load()
+    B, H, Dv = out.shape
+    if out.dtype != torch.float32 or lse.dtype != torch.float32 or tuple(lse.shape) != (B, H):
+        raise ValueError("out [B][H][Dv] and lse [B][H] must be fp32")
+    if H % N:
+        raise ValueError(f"H={H} is not a multiple of N={N}")
+    if buf is None:
+        buf = torch.empty((N, B, H // N, Dv + 4), dtype=torch.float32, device=out.device)
+    _check(lib.cp_a2a_pack(B, H, Dv, N, _ptr(out), _ptr(lse), _ptr(buf), _stream(stream)),
+           "cp_a2a_pack")
+    return buf
+
+
+def cp_lse_merge_packed(packed, Dv, out=None, lse_out=None, out_dtype=torch.float32,
+                        stream=None):
+    """Exact merge of packed partials: packed [n][rows...][Dv+4] (any strides
+    between parts, rows contiguous inside a part)."""
+    lib = _lib.load()
+    n = packed.shape[0]
+    lead = tuple(packed.shape[1:-1])
+    rows = 1
+    for x in lead:
+        rows *= x
+    if packed.dtype != torch.float32 or packed.shape[-1] != Dv + 4:
+        raise ValueError("packed must be fp32 with rows of Dv + 4")
+    if not packed[0].is_contiguous():
+        raise ValueError("rows of one part must be contiguous")
+    if not packed.is_cuda:
+        raise ValueError("libcpattn takes device tensors")
+    stride = packed.stride(0) if n > 1 else rows * (Dv + 4)
+    if out is None:
+        out = torch.empty(lead + (Dv,), dtype=out_dtype, device=packed.device)
+    if lse_out is None:
+        lse_out = torch.empty(lead, dtype=torch.float32, device=packed.device)
+    _check(lib.cp_lse_merge_packed(n, rows, Dv, ctypes.c_void_p(packed.data_ptr()), stride, _ptr(out), _dt(out),
+                                   _ptr(lse_out), _stream(stream)), "cp_lse_merge_packed")
     return out, lse_out
 
 

@@ -60,6 +60,9 @@ SIGNATURES = {
     "cp_decode_attn_partial_gqa": (_int, [ctypes.POINTER(CpGqaArgs), _vp, ctypes.c_size_t, _vp]),
     "cp_decode_attn_partial_mla": (_int, [ctypes.POINTER(CpMlaArgs), _vp, ctypes.c_size_t, _vp]),
     "cp_lse_merge": (_int, [_i32, _i64, _i32, _vp, _vp, _vp, _int, _vp, _vp]),
+    "cp_lse_correct": (_int, [_i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "cp_a2a_pack": (_int, [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "cp_lse_merge_packed": (_int, [_i32, _i64, _i32, _vp, _i64, _vp, _int, _vp, _vp]),
     "pcp_prefill_attn_causal": (_int, [ctypes.POINTER(CpPrefillArgs), _vp, ctypes.c_size_t, _vp]),
     "cp_kv_gather": (_int, [ctypes.POINTER(CpKvGatherArgs), _vp]),
     "cp_workspace_bytes": (ctypes.c_size_t, [_int, _vp]),

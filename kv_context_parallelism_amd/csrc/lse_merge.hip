@@ -54,9 +54,11 @@ __device__ __forceinline__ RowParts row_parts(const MergeDesc &m, int64_t row) {
 }
 
 // Lane-parallel merge: lane j of a kS-lane group owns float4 columns
-// j, j + kS, ... (kCols of them) of its row.  Two passes over the row's LSEs
-// (max; then weights, their sum and the weighted columns, eight parts per
-// step so that eight loads per column are in flight).
+// j, j + kS, ... (kCols of them) of its row.  One pass over the parts, eight
+// at a time: the batch's LSEs and output columns are loaded together (no
+// dependent round trip from an LSE to its output), then the running maximum
+// is raised to the batch's and the earlier sums are rescaled by
+// exp(old max - new max) -- a no-op for rows of at most eight parts.
 template <bool kBf16Out, int kS, int kCols>
 __global__ void __launch_bounds__(kThreads) merge_lanes_kernel(MergeDesc m) {
     constexpr int kRowsPerBlock = kThreads / kS;
@@ -66,56 +68,69 @@ __global__ void __launch_bounds__(kThreads) merge_lanes_kernel(MergeDesc m) {
     for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kS; row < m.rows;
          row += (int64_t)gridDim.x * kRowsPerBlock) {
         const RowParts rp = row_parts(m, row);
-        // 1. l = max_i L_i (NaN anywhere poisons the row)
         float lmax = -INFINITY;
         bool nan = false;
-        for (int i = 0; i < rp.n; ++i) {
-            const float L = rp.lp[(int64_t)i * m.l_part_stride];
-            nan |= (L != L);
-            lmax = fmaxf(lmax, L);
-        }
-        const bool empty = lmax == -INFINITY || nan;
-        // 2. a_i = exp(L_i - l), their sum, and sum_i a_i o_i
         float asum = 0.f;
         float4 acc[kCols];
 #pragma unroll
         for (int cc = 0; cc < kCols; ++cc) acc[cc] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (!empty) {
-            for (int i0 = 0; i0 < rp.n; i0 += kBatch) {
-                float a[kBatch];
+        for (int i0 = 0; i0 < rp.n; i0 += kBatch) {
+            float L[kBatch];
+            float4 o[kBatch][kCols];
 #pragma unroll
-                for (int j = 0; j < kBatch; ++j) {
-                    const float L = i0 + j < rp.n ? rp.lp[(int64_t)(i0 + j) * m.l_part_stride] : -INFINITY;
-                    a[j] = L == -INFINITY ? 0.f : expf(L - lmax);
-                    asum += a[j];
-                }
+            for (int j = 0; j < kBatch; ++j)
+                L[j] = i0 + j < rp.n ? rp.lp[(int64_t)(i0 + j) * m.l_part_stride] : -INFINITY;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const float *op = rp.op + (int64_t)(i0 + j) * m.o_part_stride;
 #pragma unroll
                 for (int cc = 0; cc < kCols; ++cc) {
                     const int c = lane_g + cc * kS;
-                    if (c < n4) {
-                        const float *op = rp.op + 4 * (int64_t)c + (int64_t)i0 * m.o_part_stride;
-                        float4 o[kBatch];
+                    o[j][cc] = i0 + j < rp.n && c < n4 ? *reinterpret_cast<const float4 *>(op + 4 * c)
+                                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+            float bmax = lmax;
 #pragma unroll
-                        for (int j = 0; j < kBatch; ++j)  // an empty part's output is never read
-                            o[j] = a[j] > 0.f ? *reinterpret_cast<const float4 *>(op + (int64_t)j * m.o_part_stride)
-                                              : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int j = 0; j < kBatch; ++j) {
+                nan |= (L[j] != L[j]);
+                bmax = fmaxf(bmax, L[j]);
+            }
+            if (bmax == -INFINITY) continue;  // every part so far is empty
+            if (bmax != lmax) {               // rescale the earlier sums to the new maximum
+                const float sc = lmax == -INFINITY ? 0.f : expf(lmax - bmax);
+                asum *= sc;
 #pragma unroll
-                        for (int j = 0; j < kBatch; ++j) {
-                            acc[cc].x += a[j] * o[j].x;
-                            acc[cc].y += a[j] * o[j].y;
-                            acc[cc].z += a[j] * o[j].z;
-                            acc[cc].w += a[j] * o[j].w;
-                        }
-                    }
+                for (int cc = 0; cc < kCols; ++cc) {
+                    acc[cc].x *= sc;
+                    acc[cc].y *= sc;
+                    acc[cc].z *= sc;
+                    acc[cc].w *= sc;
+                }
+                lmax = bmax;
+            }
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const float a = L[j] == -INFINITY ? 0.f : expf(L[j] - lmax);
+                asum += a;
+#pragma unroll
+                for (int cc = 0; cc < kCols; ++cc) {
+                    // an empty part's output is loaded but never used
+                    const float4 v = a > 0.f ? o[j][cc] : make_float4(0.f, 0.f, 0.f, 0.f);
+                    acc[cc].x += a * v.x;
+                    acc[cc].y += a * v.y;
+                    acc[cc].z += a * v.z;
+                    acc[cc].w += a * v.w;
                 }
             }
         }
-        const float inv = nan ? NAN : (asum > 0.f ? 1.f / asum : 0.f);
+        const bool empty = lmax == -INFINITY;
+        const float inv = nan ? NAN : (!empty && asum > 0.f ? 1.f / asum : 0.f);
 #pragma unroll
         for (int cc = 0; cc < kCols; ++cc) {
             const int c = lane_g + cc * kS;
             if (c >= n4) break;
-            float4 v = acc[cc];
+            float4 v = empty && !nan ? make_float4(0.f, 0.f, 0.f, 0.f) : acc[cc];
             v.x *= inv;
             v.y *= inv;
             v.z *= inv;
@@ -130,7 +145,7 @@ __global__ void __launch_bounds__(kThreads) merge_lanes_kernel(MergeDesc m) {
             }
         }
         if (m.lse_out && lane_g == 0)
-            m.lse_out[row] = nan ? NAN : (lmax == -INFINITY ? -INFINITY : lmax + logf(asum));
+            m.lse_out[row] = nan ? NAN : (empty ? -INFINITY : lmax + logf(asum));
     }
 }
 
@@ -267,13 +282,15 @@ void launch_lanes(const MergeDesc &m, hipStream_t stream) {
 
 // float4 columns -> (lanes per row, columns per lane).  Returns false (the
 // caller then uses the block kernel) when the rows are too wide, or too few
-// to give every CU a few waves of the lane layout.
+// to keep enough column loads in flight on every CU (lanes times columns per
+// lane: a row of 128 float4 columns in 64 lanes counts twice).
 template <bool kBf16Out>
 bool launch_lanes_for(const MergeDesc &m, hipStream_t stream) {
     const int n4 = m.Dv / 4;
     int S = 1;
     while (S < n4 && S < 64) S *= 2;
-    if (m.rows * S < (int64_t)device_cus() * 512) return false;
+    const int cols = (n4 + S - 1) / S;
+    if (m.rows * S * cols < (int64_t)device_cus() * 512) return false;
     if (n4 <= 1) launch_lanes<kBf16Out, 1, 1>(m, stream);
     else if (n4 <= 2) launch_lanes<kBf16Out, 2, 1>(m, stream);
     else if (n4 <= 4) launch_lanes<kBf16Out, 4, 1>(m, stream);

@@ -187,3 +187,26 @@ def test_prefill_dcp_causal_validation():
         setattr(p, field, bad)
         assert lib.pcp_prefill_attn_causal(ctypes.byref(p), None, 0, None) == 1, field
         setattr(p, field, old)
+
+
+def test_head_scatter_validation():
+    """cp_lse_correct, cp_a2a_pack and cp_lse_merge_packed check sizes,
+    ranks, head partitions, strides and alignment on the host."""
+    lib = _lib.load()
+    # rank outside [0, n_parts), Dv not a multiple of 4, misaligned output
+    assert lib.cp_lse_correct(4, 8, 16, 4, 16, 16, 16, None, None) == 1
+    assert lib.cp_lse_correct(4, 8, 16, -1, 16, 16, 16, None, None) == 1
+    assert lib.cp_lse_correct(4, 8, 18, 0, 16, 16, 16, None, None) == 2
+    assert lib.cp_lse_correct(4, 8, 16, 0, 16, 16, 20, None, None) == 1
+    assert lib.cp_lse_correct(4, 0, 16, 0, None, None, None, None, None) == 0
+    # H not a multiple of N; Dv % 4; NULL buffer
+    assert lib.cp_a2a_pack(2, 12, 16, 8, 16, 16, 16, None) == 1
+    assert lib.cp_a2a_pack(2, 16, 6, 8, 16, 16, 16, None) == 2
+    assert lib.cp_a2a_pack(2, 16, 16, 8, 16, 16, None, None) == 1
+    assert lib.cp_a2a_pack(0, 16, 16, 8, None, None, None, None) == 0
+    # part_stride below rows * (Dv + 4), or not a multiple of 4; bad dtype
+    assert lib.cp_lse_merge_packed(4, 10, 16, 16, 199, 16, 0, None, None) == 1
+    assert lib.cp_lse_merge_packed(4, 10, 16, 16, 202, 16, 0, None, None) == 1
+    assert b"part_stride" in lib.cp_last_error()
+    assert lib.cp_lse_merge_packed(4, 10, 16, 16, 200, 16, 2, None, None) == 2
+    assert lib.cp_lse_merge_packed(4, 10, 16, 24, 200, 16, 0, None, None) == 1
