@@ -242,26 +242,15 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
         const int h0 = g * G;
         cint32 *bt_row = p.bt + (int64_t)b * p.bt_stride;
 
-        // ---- query chunk c of the G heads (lane-private) ----
-        u32x4 qraw[G];
-        float qf[kBf16 ? 1 : G][4];
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const u32x4 v = load16(p.q + ((int64_t)b * p.Hq + h0 + hh) * 256 + c * 16);
-            if constexpr (kBf16) {
-                qraw[hh] = v;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) qf[hh][e] = __uint_as_float(v[e]) * p.qk_scale;
-            }
-        }
-
         // First cache row (head g) of the 16-token group at local index lb.  The
         // block id is a uniform (scalar) load, so waiting for it never waits for
         // the K/V vector loads in flight.  Groups past the segment's end map to
-        // its first group so that every address stays inside the cache.
+        // the group one tile earlier (the tile this wave is reading now, whose
+        // lines are still in its L2) or, for the segment's first tile, to its
+        // first group, so every address stays inside the cache and the
+        // unconditional prefetch past the end fetches nothing new from HBM.
         auto group_row = [&](int32_t lb) -> int64_t {
-            const int32_t gsel = lb < s1 ? lb : s0;
+            const int32_t gsel = lb < s1 ? lb : (lb - kTile >= s0 ? lb - kTile : s0);
             int32_t phys = bt_row[gsel >> p.bs_log2];
             const bool ok = phys >= 0 && (int64_t)phys < p.num_blocks;
             bad |= !ok;
@@ -289,16 +278,29 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
 #pragma unroll
             for (int e = 0; e < EPC; ++e) acc[hh][e] = 0.f;
 
-        // q has arrived before the first K/V request: the loop is then entered
-        // with the same loads in flight from the prologue and from its back
-        // edge (K then V of one tile), so the waits inside stay exact.
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        // Prologue: the first tile's K and V, then the query chunk c of the G
+        // heads (lane-private), all in flight together; then wait for all of
+        // them, so that the loop is entered with nothing in flight and the
+        // waits inside, set by its back edge (K then V of the next tile in
+        // flight), stay exact.  The query's latency overlaps the tile's.
         u32x4 kreg[kNG][4], vreg[kNG][4];
         if (s1 > s0) {
 #pragma unroll
             for (int gi = 0; gi < kNG; ++gi) rows_cur[gi] = group_row(s0 + gi * 16);
             load_tile(p.kc, rows_cur, kreg);
             load_tile(p.vc, rows_cur, vreg);
+        }
+        u32x4 qraw[G];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+            qraw[hh] = load16(p.q + ((int64_t)b * p.Hq + h0 + hh) * 256 + c * 16);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        float qf[kBf16 ? 1 : G][4];
+        if constexpr (!kBf16) {
+#pragma unroll
+            for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) qf[hh][e] = __uint_as_float(qraw[hh][e]) * p.qk_scale;
         }
         // One tile.  kTail: the segment's last tile is partial -- scores of
         // tokens past the end become -inf and their V rows (which may hold NaN
@@ -309,7 +311,7 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
             const int32_t tn = tb + kTile;
             // Block ids of the next tile, early: they are needed after the scores.
             // Full tiles always prefetch (past the segment's end the rows clamp to
-            // its first group and the reads hit the cache): a conditional
+            // the current tile and the reads hit the cache): a conditional
             // prefetch would make the compiler copy the live V registers, which
             // forces a wait on every load in flight.
             if constexpr (!kTail) {
