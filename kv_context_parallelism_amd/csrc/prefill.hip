@@ -60,11 +60,12 @@ constexpr int kTileB = kBN * kRowB;      // one K or V tile in LDS (16 KB)
 constexpr int kSlots = 2 * kTileB / 1024;  // 64-lane copies per K+V tile pair (32)
 constexpr int kMaxWaves = 8;
 constexpr float kLazy = 8.f;
-#ifndef PF_STAGES
-#define PF_STAGES 3
-#endif
-constexpr int kStages = PF_STAGES;      // LDS ring of K/V tile pairs (32 KB each)
-static_assert(kStages >= 2 && kStages * 2 * kTileB <= 160 * 1024, "ring fits the LDS");
+// A wave reads tile it's K and tile it - 1's V in iteration it, while the
+// copies of tiles it + 1 .. it + kPf are in flight: a ring of kPf + 2 K/V tile
+// pairs (32 KB each).
+constexpr int kPf = 2;
+constexpr int kStages = kPf + 2;
+static_assert(kStages * 2 * kTileB <= 160 * 1024, "ring fits the LDS");
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -273,12 +274,15 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
 
-    constexpr int kPre = 3;
+#ifndef PF_PRE
+#define PF_PRE 3
+#endif
+    constexpr int kPre = PF_PRE;
     const int ntile = kend > 0 ? (kend + kBN - 1) / kBN : 0;
     const int ntile_w = kend_w > 0 ? (kend_w + kBN - 1) / kBN : 0;  // a prefix of the tiles
     const int per_tile = kSlots / nwaves;  // this wave's copies per tile (nwaves divides 32)
 #pragma unroll
-    for (int j = 0; j < kStages - 1; ++j) {
+    for (int j = 0; j < kPf; ++j) {
         if (j < ntile) {
             const TileSrc ts = stage_rows(j * kBN);
             for (int k = 0; k < per_tile; ++k) stage_copy(j * kBN, j, ts, k);
@@ -288,7 +292,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
     // copies slots w, w + 8 (K) and w + 16, w + 24 (V), i.e. key rows
     // 16 qa + 4 (w % 4) .. +3 and 16 qb + 4 (w % 4) .. +3 of K and of V, with
     // qa = w / 4 and qb = 2 + w / 4: two block ids and one per-lane offset.
-    const bool spread_ok = kStages >= 3 && nwaves == 8;
+    const bool spread_ok = nwaves == 8;
     const int qa = wave >> 2, qb2 = 2 + (wave >> 2);
     const uint32_t off8 = [&]() {
         const int ln = lane_id_here();
@@ -307,105 +311,19 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
             return (int64_t)(t & ~15) * p.Hkv + g;
         }
     };
-    const gbyte *ksrc = kPaged ? p.kc : p.k, *vsrc = kPaged ? p.vc : p.v;
-    for (int32_t it = 0; it < ntile; ++it) {
-        const bool pre = it + kStages - 1 < ntile;
-        const int32_t jn = (it + kStages - 1) * kBN;
-        const int bn = (it + kStages - 1) % kStages;
-        const bool spread = spread_ok && pre && jn + kBN <= kend;
-        int64_t ra = 0, rb2 = 0;
-        if (spread) {  // scalar loads before the barrier that their latency then overlaps
-            ra = group_row(jn + 16 * qa);
-            rb2 = group_row(jn + 16 * qb2);
-        }
-        // tile it has landed (own copies; later tiles may still be in flight) ...
-        wait_copies_at_most(min(kStages - 2, ntile - 1 - it) * per_tile);
-        __syncthreads();  // ... for every wave; the buffer of tile it - 1 is free again
-        // the block ids are needed from here on: wait for them now, while no
-        // LDS read is in flight (the two share a wait counter)
-        asm volatile("" ::"s"(ra), "s"(rb2));
-        const uint32_t dstn = kv_lds + (uint32_t)(bn * 2 * kTileB) + (uint32_t)(wave * 1024);
-        // copy k of tile it + kStages - 1 goes after MFMA step 8 k + 7 of this tile
-        auto side = [&](int step) {
-            if ((step & 7) != 7 || !spread) return;
-            const int k = step >> 3;
-            const gbyte *src = ((k & 2) ? vsrc : ksrc) + ((k & 1) ? rb2 : ra) * (kD * 2);
-            dma16(src + off8, __builtin_amdgcn_readfirstlane(dstn + (uint32_t)(k * 8 * 1024)));
-        };
-        if (pre && !spread) {
-            const TileSrc ts = stage_rows(jn);
-            for (int k = 0; k < per_tile; ++k) stage_copy(jn, bn, ts, k);
-        }
-        if (it >= ntile_w) {  // past this wave's diagonal (uniform): copies only
-#pragma unroll
-            for (int st = 0; st < 32; ++st) side(st);
-            continue;
-        }
-        const int32_t j0 = it * kBN;
-        const int buf = it % kStages;
-        lds_u8 *tk = (lds_u8 *)(&s_kv[buf][0]);
-        lds_u8 *tv = tk + kTileB;
-
-        // Per-lane addresses (fresh lane id per tile).  Score operand of key
-        // block kb, k-step ks: row 32 kb + l % 32, chunk 2 ks + l / 32 (the key
-        // block is a constant offset: rows r and r + 32 share the swizzle).
-        // Value operand of column block db, 16-key step kk: in the 16-lane group
-        // of column half g = (l / 16) % 2, lane j reads row 16 kk + 4 (l / 32) +
-        // j / 4 and the same + 8, chunk 4 db + 2 g + (j % 4) / 2, byte 8 (j % 2)
-        // (kk is a constant offset).  The swizzle mixes the lane bits into the
-        // chunk position, so each k-step and each (column block, row half) has
-        // its own lane pointer.
-        lds_u8 *ap[8], *vp[2][4];
-        {
-            const int ln = lane_id_here();
-            const int r = ln & 31, h2 = ln >> 5;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) ap[ks] = tk + r * kRowB + 16 * ((2 * ks + h2) ^ swz(r & 15));
-            const int g = (ln >> 4) & 1, j = ln & 15;
-            const int row0 = 4 * h2 + (j >> 2), cg = 2 * g + ((j & 3) >> 1);
-#pragma unroll
-            for (int hr = 0; hr < 2; ++hr)
-#pragma unroll
-                for (int db = 0; db < 4; ++db)
-                    vp[hr][db] = tv + (row0 + 8 * hr) * kRowB + 16 * ((4 * db + cg) ^ swz(row0 + 8 * hr)) + 8 * (j & 1);
-        }
-        auto read_a = [&](int i) -> u32x4_t {  // step i: ks = i / 2, kb = i % 2
-            const int ks = i >> 1, kb = i & 1;
-            return *(__attribute__((address_space(3))) const u32x4_t *)(ap[ks] + kb * 32 * kRowB);
-        };
-        auto read_v = [&](int i) -> u32x4_t {  // step i: kk = i / 4, db = i % 4
-            const int kk = i >> 2, db = i & 3;
-            lds_u8 *va0 = vp[0][db] + kk * 16 * kRowB;
-            lds_u8 *va1 = vp[1][db] + kk * 16 * kRowB;
-            const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4_t *)(va0));
-            const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) i16x4_t *)(va1));
-            const u32x2_t w0 = __builtin_bit_cast(u32x2_t, t0), w1 = __builtin_bit_cast(u32x2_t, t1);
-            return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
-        };
-
-        // ---- scores S^T[key][row]: 2 key blocks x 8 k-steps, key blocks interleaved ----
-        // (raw dot products; the scale is applied inside the exponent below)
-        f32x16_t sc[2];
-        {
-            u32x4_t abuf[kPre];
-#pragma unroll
-            for (int i = 0; i < kPre; ++i) abuf[i] = read_a(i);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const u32x4_t a = abuf[i % kPre];
-                if (i + kPre < 16) abuf[i % kPre] = read_a(i + kPre);
-                const int ks = i >> 1, kb = i & 1;
-                f32x16_t zero;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) zero[e] = 0.f;
-                sc[kb] = mfma32(a, qb_reg[ks], ks == 0 ? zero : sc[kb]);
-                __builtin_amdgcn_sched_barrier(0);
-                side(i);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
+    // Ping-pong.  Iteration it is one MFMA block -- the value product of tile
+    // it - 1, then the scores of tile it -- and the softmax of tile it (VALU).
+    // The first wave of each SIMD (waves 0-3) runs the block and then the
+    // softmax; the second (waves 4-7) holds its scores over the barrier and
+    // runs the softmax of tile it - 1 first.  After every barrier one wave of
+    // a SIMD is thus in its VALU phase while the other issues MFMAs.
+    const bool pong = (wave >> 2) & 1;
+    f32x16_t sc[2];   // scores S^T[key][row] of the last scored tile (raw dot products)
+    u32x4_t pa[4];    // its probabilities as the A operand of the value product
+    // online softmax of tile t (scores in sc) -> pa; rescales o when the
+    // reference maximum is raised
+    auto softmax = [&](int32_t t) {
+        const int32_t j0 = t * kBN;
         // lane holds keys j0 + 32 kb + acc_row(e, hf) for query row i0w + l % 32.
         // Only tiles that reach past the visible keys or straddle the diagonal
         // need a mask (a uniform test).
@@ -443,28 +361,104 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
         // p = 2^(s * scale - m_ref); a row with no visible key yet keeps the
         // reference at -inf and shifts by 0.  (The denominator is summed in
         // fp32: the LSE needs more than the bf16 precision of the weights.)
-        u32x4_t pa[4];
-        {
-            const float ms = m_ref == -INFINITY ? 0.f : m_ref;
-            float ps = 0.f;
+        const float ms = m_ref == -INFINITY ? 0.f : m_ref;
+        float ps = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    sc[kb][e] = fast_exp2(fmaf(sc[kb][e], p.qk_scale, -ms));
-                    ps += sc[kb][e];
-                }
-            l_run += ps;
-            // P as the A operand of 16-key step kk: elements 8 (kk % 2) .. +7 of
-            // key block kk / 2, in order
+            for (int e = 0; e < 16; ++e) {
+                sc[kb][e] = fast_exp2(fmaf(sc[kb][e], p.qk_scale, -ms));
+                ps += sc[kb][e];
+            }
+        l_run += ps;
+        // P as the A operand of 16-key step kk: elements 8 (kk % 2) .. +7 of
+        // key block kk / 2, in order
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
+        for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    pa[kk][i] = pack_bf16x2(sc[kk >> 1][8 * (kk & 1) + 2 * i], sc[kk >> 1][8 * (kk & 1) + 2 * i + 1]);
+            for (int i = 0; i < 4; ++i)
+                pa[kk][i] = pack_bf16x2(sc[kk >> 1][8 * (kk & 1) + 2 * i], sc[kk >> 1][8 * (kk & 1) + 2 * i + 1]);
+    };
+
+    // Per-lane LDS byte offsets inside a tile, computed once.  Score operand of
+    // key block kb, k-step ks: row 32 kb + l % 32, chunk 2 ks + l / 32 (the key
+    // block is a constant offset: rows r and r + 32 share the swizzle).  Value
+    // operand of column block db, 16-key step kk: in the 16-lane group of
+    // column half g = (l / 16) % 2, lane j reads row 16 kk + 4 (l / 32) + j / 4
+    // and the same + 8, chunk 4 db + 2 g + (j % 4) / 2, byte 8 (j % 2) (kk is a
+    // constant offset).  The swizzle mixes the lane bits into the chunk
+    // position, so each k-step and each (column block, row half) has its own
+    // offset.
+    uint32_t aoff[8], voff[2][4];
+    {
+        const int r = lane & 31, h2 = lane >> 5;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) aoff[ks] = r * kRowB + 16 * ((2 * ks + h2) ^ swz(r & 15));
+        const int g2 = (lane >> 4) & 1, j = lane & 15;
+        const int row0 = 4 * h2 + (j >> 2), cg = 2 * g2 + ((j & 3) >> 1);
+#pragma unroll
+        for (int hr = 0; hr < 2; ++hr)
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                voff[hr][db] = (row0 + 8 * hr) * kRowB + 16 * ((4 * db + cg) ^ swz(row0 + 8 * hr)) + 8 * (j & 1);
+    }
+    const gbyte *ksrc = kPaged ? p.kc : p.k, *vsrc = kPaged ? p.vc : p.v;
+    for (int32_t it = 0; it <= ntile; ++it) {  // it == ntile: the last value product only
+        const bool pre = it + kPf < ntile;
+        const int32_t jn = (it + kPf) * kBN;
+        const int bn = (it + kPf) % kStages;
+        const bool spread = spread_ok && pre && jn + kBN <= kend;
+        int64_t ra = 0, rb2 = 0;
+        if (spread) {  // scalar loads before the barrier that their latency then overlaps
+            ra = group_row(jn + 16 * qa);
+            rb2 = group_row(jn + 16 * qb2);
         }
-        // ---- values: O[row][d] += P[row][key] V[key][d], 4 column blocks x 4 key steps ----
-        {
+        // tile it has landed (own copies; later tiles may still be in flight) ...
+        wait_copies_at_most(min(kPf - 1, ntile - 1 - it) * per_tile);
+        __syncthreads();  // ... for every wave; the buffer of tile it - 2 is free again
+        // the block ids are needed from here on: wait for them now, while no
+        // LDS read is in flight (the two share a wait counter)
+        asm volatile("" ::"s"(ra), "s"(rb2));
+        const uint32_t dstn = kv_lds + (uint32_t)(bn * 2 * kTileB) + (uint32_t)(wave * 1024);
+        // copy k of tile it + kPf goes after MFMA step 8 k + 7 of this block
+        auto side = [&](int step) {
+            if ((step & 7) != 7 || !spread) return;
+            const int k = step >> 3;
+            const gbyte *src = ((k & 2) ? vsrc : ksrc) + ((k & 1) ? rb2 : ra) * (kD * 2);
+            dma16(src + off8, __builtin_amdgcn_readfirstlane(dstn + (uint32_t)(k * 8 * 1024)));
+        };
+        if (pre && !spread) {
+            const TileSrc ts = stage_rows(jn);
+            for (int k = 0; k < per_tile; ++k) stage_copy(jn, bn, ts, k);
+        }
+        const bool do_pv = it >= 1 && it - 1 < ntile_w;   // value product of tile it - 1
+        const bool do_s = it < ntile_w;                  // scores of tile it
+        if (!do_pv && !do_s) {  // past this wave's diagonal (uniform): copies only
+#pragma unroll
+            for (int st = 0; st < 32; ++st) side(st);
+            continue;
+        }
+        if (pong && do_pv) softmax(it - 1);
+
+        // ---- values of tile it - 1: O[row][d] += P[row][key] V[key][d], 4 column blocks x 4 key steps ----
+        if (do_pv) {
+            lds_u8 *tv = (lds_u8 *)(&s_kv[(it - 1) % kStages][0]) + kTileB;
+            lds_u8 *vp[2][4];
+#pragma unroll
+            for (int hr = 0; hr < 2; ++hr)
+#pragma unroll
+                for (int db = 0; db < 4; ++db) vp[hr][db] = tv + voff[hr][db];
+            auto read_v = [&](int i) -> u32x4_t {  // step i: kk = i / 4, db = i % 4
+                const int kk = i >> 2, db = i & 3;
+                lds_u8 *va0 = vp[0][db] + kk * 16 * kRowB;
+                lds_u8 *va1 = vp[1][db] + kk * 16 * kRowB;
+                const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(va0));
+                const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(va1));
+                const u32x2_t w0 = __builtin_bit_cast(u32x2_t, t0), w1 = __builtin_bit_cast(u32x2_t, t1);
+                return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
+            };
             u32x4_t vbuf[kPre];
 #pragma unroll
             for (int i = 0; i < kPre; ++i) vbuf[i] = read_v(i);
@@ -475,9 +469,44 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
                 const int kk = i >> 2, db = i & 3;
                 o[db] = mfma32(pa[kk], vb, o[db]);
                 __builtin_amdgcn_sched_barrier(0);
+                side(i);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+            for (int st = 0; st < 16; ++st) side(st);
+        }
+        // ---- scores of tile it: 2 key blocks x 8 k-steps, key blocks interleaved ----
+        // (raw dot products; the scale is applied inside the exponent)
+        if (do_s) {
+            lds_u8 *tk = (lds_u8 *)(&s_kv[it % kStages][0]);
+            lds_u8 *ap[8];
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) ap[ks] = tk + aoff[ks];
+            auto read_a = [&](int i) -> u32x4_t {  // step i: ks = i / 2, kb = i % 2
+                const int ks = i >> 1, kb = i & 1;
+                return *(__attribute__((address_space(3))) const u32x4_t *)(ap[ks] + kb * 32 * kRowB);
+            };
+            u32x4_t abuf[kPre];
+#pragma unroll
+            for (int i = 0; i < kPre; ++i) abuf[i] = read_a(i);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const u32x4_t a = abuf[i % kPre];
+                if (i + kPre < 16) abuf[i % kPre] = read_a(i + kPre);
+                const int ks = i >> 1, kb = i & 1;
+                f32x16_t zero;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) zero[e] = 0.f;
+                sc[kb] = mfma32(a, qb_reg[ks], ks == 0 ? zero : sc[kb]);
+                __builtin_amdgcn_sched_barrier(0);
                 side(16 + i);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            if (!pong) softmax(it);
+        } else {
+#pragma unroll
+            for (int st = 16; st < 32; ++st) side(st);
         }
     }
 
