@@ -97,7 +97,19 @@ def test_gqa_deterministic_and_workspace():
     out = torch.empty(3, w.Hq, w.D, device="cuda")
     lse = torch.empty(3, w.Hq, device="cuda")
     args = cp.gqa_args(case.q, sh["kc"], sh["vc"], sh["bt_dev"], sh["ll_dev"], w.scale, out, lse)
-    assert cp.cp_workspace_bytes(cp.CP_OP_DECODE_GQA, args) > 0
+    need = cp.cp_workspace_bytes(cp.CP_OP_DECODE_GQA, args)
+    assert need > 0
+    # the workspace need not be initialised: random bytes, all ones, all zeros
+    g = torch.Generator(device="cuda").manual_seed(7)
+    fills = [torch.randint(0, 256, (need,), dtype=torch.uint8, device="cuda", generator=g),
+             torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda"),
+             torch.zeros(need, dtype=torch.uint8, device="cuda")]
+    ref = cp.cp_decode_attn_partial_gqa(case.q, sh["kc"], sh["vc"], sh["bt_dev"], sh["ll_dev"],
+                                        w.scale)
+    for ws in fills:
+        o, l = cp.cp_decode_attn_partial_gqa(case.q, sh["kc"], sh["vc"], sh["bt_dev"],
+                                             sh["ll_dev"], w.scale, workspace=ws)
+        assert torch.equal(o, ref[0]) and torch.equal(l, ref[1])
     small = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(cp.CpError):
         # an explicit workspace that is too small is rejected before launch
