@@ -10,11 +10,16 @@
 // first Dv = 512 columns.
 //
 // Design (a dense contraction: up to 128 heads x 576 against every cached row):
-//   * one workgroup = 8 waves (two per SIMD), wave w owning query heads
-//     16w .. 16w+15; every latent tile staged in LDS feeds all 128 heads.  A
-//     wave's accumulators (16 x 512 fp32 outputs, 16 x 32 scores) and its
-//     queries fit its 256 VGPRs; the file is compiled with MFMA results in
-//     VGPRs so that the softmax rescale updates them in place;
+//   * one workgroup = 8 waves (two per SIMD); every latent tile staged in LDS
+//     feeds all 128 heads.  Scores are split by heads: wave w computes the
+//     scores and the softmax of query heads 16w .. 16w+15 (its queries stay in
+//     registers for the segment).  The value product is split by columns:
+//     wave w accumulates O[h][64 w .. 64 w + 63] for every head h, so each
+//     value column is read from LDS by one wave only.  The probabilities pass
+//     between the two through LDS (a second barrier per tile), together with
+//     each head's rescale factor.  The accumulators (128 x 64 fp32 outputs,
+//     16 x 32 scores) and the queries fit a wave's 256 VGPRs; the file is
+//     compiled with MFMA results in VGPRs so that rescales update them in place;
 //   * 32-token latent tiles go HBM -> LDS by global_load_lds (no registers),
 //     triple-buffered: two tiles are in flight while the third is consumed.
 //     The copies are issued from inline asm and waited for with explicit
@@ -24,13 +29,11 @@
 //     XOR-swizzled by (t / 2) % 8: both LDS read patterns below are free of
 //     bank conflicts;
 //   * scores S^T = C Q^T on v_mfma_f32_16x16x32_bf16 (A = latent rows from
-//     LDS, B = the wave's 16 queries, held in registers for the segment); the
-//     score tile comes out in the A-operand layout of the value product (the
-//     token order inside the 32-token k-step is permuted identically on both
-//     operands);
-//   * values O = P V with the V operand read by ds_read_b64_tr_b16 (transposing
-//     LDS read);
-//   * both products are software-pipelined by hand, three LDS operands ahead;
+//     LDS, B = the wave's 16 queries); the probabilities are stored per head
+//     in the k order of the value product;
+//   * values O = P V on v_mfma_f32_32x32x16_bf16, the V operand read by
+//     ds_read_b64_tr_b16 (transposing LDS read), the P operand one 16-byte
+//     LDS read per 32-head block;
 //   * online softmax in the exp2 domain with a lazily updated reference
 //     maximum: the output is rescaled only when a tile's maximum exceeds the
 //     reference by more than 2^8, which keeps every probability <= 256 and the
@@ -58,12 +61,13 @@ constexpr int kRowB = kDk * 2;          // LDS row: 1152 bytes = 72 chunks of 16
 constexpr int kRowC = kRowB / 16;
 constexpr int kTileB = kT * kRowB;      // 36,864 bytes
 constexpr int kKs = kDk / 32;           // 18 k-steps of the score MFMA
-constexpr int kVb = kDv / 16;           // 32 value-column blocks
 constexpr int kMaxB = 4096;
 constexpr int kWaves = 8;               // 16 heads per wave, two waves per SIMD
 constexpr int kHeadsWg = 16 * kWaves;   // 128
 constexpr int kThreads = 64 * kWaves;
 constexpr float kLazy = 8.f;            // rescale only past 2^8
+constexpr int kPRow = 80;               // LDS row of one head's 32 probabilities (64 + 16 bytes)
+constexpr int kVcW = kDv / kWaves;      // value columns of one wave in the value product (64)
 
 // copies per tile: bf16 goes straight into the tile (36 copies of 64 chunks),
 // fp8 into a raw ring (36 chunks per row, 18 copies)
@@ -94,6 +98,16 @@ struct MlaParams {
 
 __device__ __forceinline__ f32x4_t mfma16(const u32x4_t &a, const u32x4_t &b, const f32x4_t &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// D (32 x 32) += A (32 x 16) B (16 x 32); lane l holds A[l % 32][8 (l / 32) + e],
+// B[8 (l / 32) + e][l % 32] (e = 0 .. 7) and D[8 (e / 4) + 4 (l / 32) + e % 4][l % 32]
+// (e = 0 .. 15).
+__device__ __forceinline__ f32x16_t mfma32(const u32x4_t &a, const u32x4_t &b, const f32x16_t &c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
@@ -165,6 +179,12 @@ __global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t s_raw[kRawBufs][kFp8 ? kT * kDk : 16];
     __shared__ int32_t s_pref[kMaxB + 1];
     __shared__ int32_t s_wsum[kWaves];
+    // probabilities of the tile, [head][32 tokens in value-product k order]
+    // (rows padded to 80 bytes: the 16-byte reads of 16 rows hit distinct banks)
+    __shared__ __attribute__((aligned(16))) uint8_t s_p[kHeadsWg * kPRow];
+    __shared__ __attribute__((aligned(16))) float s_alpha[kHeadsWg];  // rescale of each head's rows
+    __shared__ __attribute__((aligned(16))) float s_linv[kHeadsWg];   // 1 / row sum at the end
+    __shared__ __attribute__((aligned(8))) uint8_t s_flag[kWaves];    // a head of wave w rescaled
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -268,7 +288,15 @@ __global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
         // last token (finite data; their probability is forced to 0).  Copy sl
         // fills destination chunks 64 sl .. 64 sl + 63 of the tile; the source
         // chunk of destination position p in row t is p ^ swz(t).
-        auto issue_tile = [&](int32_t it) {
+        // A tile's copies: the cache rows of its two 16-token halves (scalar
+        // block-table loads), then this wave's copies, copy i being slot
+        // sl = wave + 8 i.
+        struct TileRows {
+            int64_t r0, r1;  // cache rows of the tile's first token and of token 16
+            int32_t nval;    // real tokens of the tile
+            int32_t it;      // tile index (ring position)
+        };
+        auto tile_rows = [&](int32_t it) -> TileRows {
             const int32_t tb = s0 + it * kT;
             const int32_t nval = min(kT, s1 - tb);
             auto row_of = [&](int32_t tok) -> int64_t {
@@ -278,34 +306,45 @@ __global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
                 phys = ok ? phys : 0;
                 return ((int64_t)phys << p.bs_log2) + (tok & (bs - 1));
             };
-            const int64_t r0 = row_of(tb);
-            const int64_t r1 = row_of(tb + min(16, nval - 1));  // == r0 + 16 within one block
+            TileRows tr;
+            tr.r0 = row_of(tb);
+            tr.r1 = row_of(tb + min(16, nval - 1));  // == r0 + 16 within one block
+            tr.nval = nval;
+            tr.it = it;
+            return tr;
+        };
+        constexpr int kSlots = kFp8 ? kRawSlots : kBfSlots;
+        constexpr int kCopies = (kSlots + kWaves - 1) / kWaves;  // per wave, at most
+        auto issue_copy = [&](const TileRows &tr, int i) {
+            const int sl = wave + kWaves * i;
+            if (sl >= kSlots) return;
+            const int64_t r0 = tr.r0, r1 = tr.r1;
+            const int32_t nval = tr.nval;
             if constexpr (kFp8) {
-                const uint32_t dst = raw_lds + (uint32_t)((it % 3) * (kT * kDk));
-#pragma unroll
-                for (int i = 0; i < (kRawSlots + kWaves - 1) / kWaves; ++i) {
-                    const int sl = wave + kWaves * i;
-                    if (sl >= kRawSlots) break;
-                    const int c = sl * 64 + lane_id_here();
-                    const int tt = min(c / (kDk / 16), nval - 1), ch = c % (kDk / 16);
-                    const int64_t row = (tt < 16 ? r0 : r1 - 16) + tt;
-                    dma16(p.kv + row * kDk + ch * 16,
-                          __builtin_amdgcn_readfirstlane(dst + sl * 1024));
-                }
+                const uint32_t dst = raw_lds + (uint32_t)((tr.it % 3) * (kT * kDk));
+                const int c = sl * 64 + lane_id_here();
+                const int tt = min(c / (kDk / 16), nval - 1), ch = c % (kDk / 16);
+                const int64_t row = (tt < 16 ? r0 : r1 - 16) + tt;
+                dma16(p.kv + row * kDk + ch * 16, __builtin_amdgcn_readfirstlane(dst + sl * 1024));
             } else {
-                const uint32_t dst = kv_lds + (uint32_t)((it % 3) * kTileB);
-#pragma unroll
-                for (int i = 0; i < (kBfSlots + kWaves - 1) / kWaves; ++i) {
-                    const int sl = wave + kWaves * i;
-                    if (sl >= kBfSlots) break;
-                    const int c = sl * 64 + lane_id_here();  // destination chunk in the tile
-                    const int t = c / kRowC, pos = c - t * kRowC;
-                    const int tt = min(t, nval - 1);
-                    const int64_t rbase = tt < 16 ? r0 : r1 - 16;
-                    dma16(p.kv + (rbase + tt) * kRowB + (pos ^ swz(t)) * 16,
-                          __builtin_amdgcn_readfirstlane(dst + sl * 1024));
-                }
+                const uint32_t dst = kv_lds + (uint32_t)((tr.it % 3) * kTileB);
+                const int c = sl * 64 + lane_id_here();  // destination chunk in the tile
+                const int t = c / kRowC, pos = c - t * kRowC;
+                const int tt = min(t, nval - 1);
+                const int64_t rbase = tt < 16 ? r0 : r1 - 16;
+                dma16(p.kv + (rbase + tt) * kRowB + (pos ^ swz(t)) * 16,
+                      __builtin_amdgcn_readfirstlane(dst + sl * 1024));
             }
+        };
+        // Cache rows of the tile's tokens: a 32-token tile spans at most two
+        // blocks (bs >= 16).  Tokens past the segment's end reuse the row of its
+        // last token (finite data; their probability is forced to 0).  Copy sl
+        // fills destination chunks 64 sl .. 64 sl + 63 of the tile; the source
+        // chunk of destination position p in row t is p ^ swz(t).
+        auto issue_tile = [&](int32_t it) {
+            const TileRows tr = tile_rows(it);
+#pragma unroll
+            for (int i = 0; i < kCopies; ++i) issue_copy(tr, i);
         };
         // fp8: widen raw tile `it` into bf16 buffer it % 2 (all threads)
         auto widen_tile = [&](int32_t it) {
@@ -339,48 +378,45 @@ __global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
         };
 
         float m_ref = -INFINITY, l_run = 0.f;  // per head lane % 16 (same in all four groups)
-        f32x4_t o[kVb];
+        // The value product is split by columns: wave w accumulates
+        // O[h][64 w .. 64 w + 63] for every head h, in 32 x 32 blocks
+        // o[hb][cb] = O[32 hb + 8 (e / 4) + 4 (l / 32) + e % 4][64 w + 32 cb + l % 32].
+        f32x16_t o[4][2];
 #pragma unroll
-        for (int vb = 0; vb < kVb; ++vb) o[vb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[hb][cb][e] = 0.f;
+        // All four 32-head blocks are computed whatever H is: rows of heads
+        // >= H (probabilities never written) are never stored.
+        constexpr int nhb = 4;
 
-        // Both products are software-pipelined by hand: the LDS operand of step
-        // i + kPre is requested before the MFMA of step i, and a scheduling
-        // barrier after each step keeps the compiler from hoisting further
-        // reads into registers.
+        // Scores and softmax of the wave's 16 heads (active waves).  The
+        // probabilities go to s_p in the k order of the value product; the
+        // rescale factors of the wave's heads to s_alpha and whether any head
+        // was rescaled to s_flag[wave].  The score product is pipelined by
+        // hand, three LDS operands ahead, with a scheduling barrier per step.
         constexpr int kPre = 3;
-        auto compute_tile = [&](int32_t it, const uint8_t *tile) {
+        auto scores_softmax = [&](int32_t it, const uint8_t *tile) {
             const int32_t tb = s0 + it * kT;
-            // Per-lane LDS addresses (16-lane group G = lane / 16, j = lane % 16),
+            // Per-lane addresses (16-lane group G = lane / 16, j = lane % 16),
             // recomputed per tile from a fresh lane id.  Score operand of half hf,
-            // k-step ks: row 16 hf + j, chunk 4 ks + G.  Value operand of column
-            // block vb: rows 4 G + j / 4 (and + 16), chunk 2 vb + (j % 4) / 2, byte
-            // 8 (j % 2).  Rows r and r + 16 share swz(r), so the + 16 row halves
-            // are a constant offset; the swizzle acts on the chunk's low 3 bits.
+            // k-step ks: row 16 hf + j, chunk 4 ks + G.  Rows r and r + 16 share
+            // swz(r), so the + 16 row halves are a constant offset; the swizzle
+            // acts on the chunk's low 3 bits.
             lds_u8 *t3 = (lds_u8 *)(tile);
-            lds_u8 *ap[2], *vp[4];
+            lds_u8 *ap[2];
             {
                 const int ln = lane_id_here();
                 const int G = ln >> 4, j = ln & 15;
 #pragma unroll
                 for (int k2 = 0; k2 < 2; ++k2) ap[k2] = t3 + j * kRowB + 16 * ((4 * k2 + G) ^ swz(j));
-                const int vr = 4 * G + (j >> 2);
-#pragma unroll
-                for (int v4 = 0; v4 < 4; ++v4)
-                    vp[v4] = t3 + vr * kRowB + 16 * ((2 * v4 + ((j & 3) >> 1)) ^ swz(vr)) + 8 * (j & 1);
             }
             auto read_a = [&](int i) -> u32x4_t {  // step i: half i % 2, k-step i / 2
                 const int hf = i & 1, ks = i >> 1;
                 return *(__attribute__((address_space(3))) const u32x4_t *)(
                     ap[ks & 1] + hf * 16 * kRowB + 128 * (ks >> 1));
-            };
-            auto read_v = [&](int vb) -> u32x4_t {
-                lds_u8 *va = vp[vb & 3] + 128 * (vb >> 2);
-                const i16x4_t t0 =
-                    __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t *)(va));
-                const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) i16x4_t *)(va + 16 * kRowB));
-                const u32x2_t w0 = __builtin_bit_cast(u32x2_t, t0), w1 = __builtin_bit_cast(u32x2_t, t1);
-                return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
             };
 
             // ---- scores S^T[t][h]: two 16-token halves x 18 k-steps, the halves
@@ -407,29 +443,23 @@ __global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
             for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float s = sc[hf][e] * p.qk_scale;
-                    if (16 * hf + e >= lim) s = -INFINITY;
-                    sc[hf][e] = s;
-                    mt = fmaxf(mt, s);
+                    float sv = sc[hf][e] * p.qk_scale;
+                    if (16 * hf + e >= lim) sv = -INFINITY;
+                    sc[hf][e] = sv;
+                    mt = fmaxf(mt, sv);
                 }
             mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
             mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            float alpha = 1.f;
+            int resc = 0;
             if (it == 0) {
                 m_ref = mt;
             } else if (__any(mt > m_ref + kLazy)) {
                 const float mn = fmaxf(m_ref, mt);
-                const float alpha = fast_exp2(m_ref - mn);
+                alpha = fast_exp2(m_ref - mn);
                 m_ref = mn;
                 l_run *= alpha;
-                // output row e of this lane is head 4 G + e
-                const int gb = (lane_id_here() >> 4) * 4;
-                float ar[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) ar[e] = __shfl(alpha, gb + e, 64);
-#pragma unroll
-                for (int vb = 0; vb < kVb; ++vb)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[vb][e] *= ar[e];
+                resc = 1;
             }
             float ps = 0.f;
 #pragma unroll
@@ -440,27 +470,96 @@ __global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
                     ps += sc[hf][e];
                 }
             l_run += ps;
-            // P as the A operand: k = 8 G + e <-> tokens 4 G + e (e < 4) and
-            // 16 + 4 G + e - 4
-            u32x4_t pa;
-            pa[0] = pack_bf16x2(sc[0][0], sc[0][1]);
-            pa[1] = pack_bf16x2(sc[0][2], sc[0][3]);
-            pa[2] = pack_bf16x2(sc[1][0], sc[1][1]);
-            pa[3] = pack_bf16x2(sc[1][2], sc[1][3]);
-
-            // ---- values: O[h][v] += P[h][t] V[t][v], 16 columns per MFMA ----
+            // token 16 hf + 4 G + e sits at k position 16 hf + 8 (G % 2) + 4 (G / 2) + e
             {
-                u32x4_t vbuf[kPre];
+                uint8_t *prow = s_p + (h0 + (lane & 15)) * kPRow + 2 * (8 * (G & 1) + 4 * (G >> 1));
 #pragma unroll
-                for (int i = 0; i < kPre; ++i) vbuf[i] = read_v(i);
+                for (int hf = 0; hf < 2; ++hf)
+                    *reinterpret_cast<u32x2_t *>(prow + 32 * hf) =
+                        u32x2_t{pack_bf16x2(sc[hf][0], sc[hf][1]), pack_bf16x2(sc[hf][2], sc[hf][3])};
+            }
+            if (lane < 16) s_alpha[h0 + lane] = alpha;
+            if (lane == 0) s_flag[wave] = (uint8_t)resc;
+        };
+
+        // Value product of the tile for this wave's 64 columns and every head:
+        // O[h][c] += P[h][t] V[t][c] on 32 x 32 x 16 MFMAs, two 16-token k-steps.
+        // V (B operand) is read by ds_read_b64_tr_b16: in the 16-lane group of
+        // column half g = (l / 16) % 2, lane j reads rows 16 kk + 4 (l / 32) +
+        // j / 4 and the same + 8, chunk 8 w + 4 cb + 2 g + (j % 4) / 2, byte
+        // 8 (j % 2); the probabilities (A operand) are one 16-byte read per
+        // (head block, k-step) from s_p, whose k order matches those rows.
+        auto value_product = [&](const uint8_t *tile) {
+            // rescale the rows of every head whose owner raised its reference maximum
+            const uint64_t flags = *reinterpret_cast<const uint64_t *>(s_flag);
+            if (flags != 0) {
+                const int h2 = lane >> 5;
 #pragma unroll
-                for (int vb = 0; vb < kVb; ++vb) {
-                    const u32x4_t v = vbuf[vb % kPre];
-                    if (vb + kPre < kVb) vbuf[vb % kPre] = read_v(vb + kPre);
-                    o[vb] = mfma16(pa, v, o[vb]);
+                for (int hb = 0; hb < 4; ++hb) {
+                    if (hb >= nhb) break;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 a4 = *reinterpret_cast<const float4 *>(s_alpha + 32 * hb + 8 * q + 4 * h2);
+#pragma unroll
+                        for (int cb = 0; cb < 2; ++cb) {
+                            o[hb][cb][4 * q + 0] *= a4.x;
+                            o[hb][cb][4 * q + 1] *= a4.y;
+                            o[hb][cb][4 * q + 2] *= a4.z;
+                            o[hb][cb][4 * q + 3] *= a4.w;
+                        }
+                    }
+                }
+            }
+            lds_u8 *t3 = (lds_u8 *)(tile);
+            lds_u8 *vp[2][2];  // [cb][row half]
+            lds_u8 *pp;
+            {
+                const int ln = lane_id_here();
+                const int h2 = ln >> 5, g2 = (ln >> 4) & 1, j = ln & 15;
+                const int row0 = 4 * h2 + (j >> 2), cg = 2 * g2 + ((j & 3) >> 1);
+#pragma unroll
+                for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+                    for (int hr = 0; hr < 2; ++hr) {
+                        const int r = row0 + 8 * hr;
+                        vp[cb][hr] = t3 + r * kRowB + 16 * (8 * wave + ((4 * cb + cg) ^ swz(r))) + 8 * (j & 1);
+                    }
+                pp = (lds_u8 *)(s_p) + (ln & 31) * kPRow + 16 * h2;
+            }
+            auto read_v = [&](int cb, int kk) -> u32x4_t {  // rows + 16 kk share the swizzle
+                const i16x4_t t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(vp[cb][0] + kk * 16 * kRowB));
+                const i16x4_t t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) i16x4_t *)(vp[cb][1] + kk * 16 * kRowB));
+                const u32x2_t w0 = __builtin_bit_cast(u32x2_t, t0), w1 = __builtin_bit_cast(u32x2_t, t1);
+                return u32x4_t{w0[0], w0[1], w1[0], w1[1]};
+            };
+            auto read_p = [&](int hb, int kk) -> u32x4_t {
+                return *(__attribute__((address_space(3))) const u32x4_t *)(pp + hb * 32 * kPRow + 32 * kk);
+            };
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const u32x4_t v0 = read_v(0, kk), v1 = read_v(1, kk);
+                u32x4_t pn = read_p(0, kk);
+#pragma unroll
+                for (int hb = 0; hb < 4; ++hb) {
+                    if (hb >= nhb) break;
+                    const u32x4_t pa = pn;
+                    if (hb + 1 < 4 && hb + 1 < nhb) pn = read_p(hb + 1, kk);
+                    o[hb][0] = mfma32(pa, v0, o[hb][0]);
+                    o[hb][1] = mfma32(pa, v1, o[hb][1]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
+        };
+        auto compute_tile = [&](int32_t it, const uint8_t *tile) {
+            if (active) {
+                scores_softmax(it, tile);
+            } else if (lane == 0) {
+                s_flag[wave] = 0;
+            }
+            __syncthreads();  // every head's probabilities and rescale factors are in LDS
+            value_product(tile);
         };
 
         if constexpr (kFp8) {
@@ -478,7 +577,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
                 __syncthreads();  // widened tile it complete; buffers of it - 1 free
                 if (it + 3 < ntile) issue_tile(it + 3);
                 if (it + 1 < ntile) widen_tile(it + 1);
-                if (active) compute_tile(it, s_kv[it % 2]);
+                compute_tile(it, s_kv[it % 2]);
             }
         } else {
             if (ntile > 0) issue_tile(0);
@@ -487,7 +586,7 @@ __global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
                 wait_all_but_one_tile<kBfSlots>(it + 1 < ntile, wave);
                 __syncthreads();  // tile it landed for all waves; buffer of it - 1 free
                 if (it + 2 < ntile) issue_tile(it + 2);
-                if (active) compute_tile(it, s_kv[it % 3]);
+                compute_tile(it, s_kv[it % 3]);
             }
         }
 
@@ -497,24 +596,38 @@ __global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
         lt += __shfl_xor(lt, 32, 64);
         bad = __syncthreads_or(bad);  // also: every wave is done with the LDS ring
         const bool empty = ntile == 0;
-        const float inv_h = bad ? NAN : (empty ? 0.f : p.v_scale / lt);
         if (active) {
             const int ln = lane_id_here();
-            const int gb = (ln >> 4) * 4, lc = ln & 15;
-            float *o_dst = p.ws_o + (slot * p.H + h0) * kDv + lc;
-            float iv[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) iv[e] = __shfl(inv_h, gb + e, 64);
-#pragma unroll
-            for (int vb = 0; vb < kVb; ++vb) {
-                const f32x4_t ov = o[vb];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (h0 + gb + e < p.H) o_dst[(gb + e) * kDv + vb * 16] = ov[e] * iv[e];
+            if (ln < 16) {
+                s_linv[h0 + ln] = bad ? NAN : (empty ? 0.f : p.v_scale / lt);
+                if (h0 + ln < p.H)
+                    p.ws_l[slot * p.H + h0 + ln] =
+                        bad ? NAN : (empty ? -INFINITY : (m_ref + fast_log2(lt)) * kLn2);
             }
-            if (ln < 16 && h0 + ln < p.H)
-                p.ws_l[slot * p.H + h0 + ln] =
-                    bad ? NAN : (empty ? -INFINITY : (m_ref + fast_log2(lt)) * kLn2);
+        }
+        __syncthreads();  // every head's 1 / row sum is in LDS
+        {
+            const int ln = lane_id_here();
+            const int h2 = ln >> 5;
+            float *o_dst = p.ws_o + slot * p.H * kDv + kVcW * wave + (ln & 31);
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) {
+                if (hb >= nhb) break;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 iv = *reinterpret_cast<const float4 *>(s_linv + 32 * hb + 8 * q + 4 * h2);
+                    const float ivs[4] = {iv.x, iv.y, iv.z, iv.w};
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int h = 32 * hb + 8 * q + 4 * h2 + r;
+                        if (h < p.H) {
+#pragma unroll
+                            for (int cb = 0; cb < 2; ++cb)
+                                o_dst[(int64_t)h * kDv + 32 * cb] = o[hb][cb][4 * q + r] * ivs[r];
+                        }
+                    }
+                }
+            }
         }
         cc += nseg;
     }
