@@ -175,6 +175,24 @@ def attention(q, k, v, *, key_begin, key_end, scale: float, q_dtype: str, kv_dty
     return out, lse
 
 
+def decode_mtp(q, k, v, *, L: int, scale: float, q_dtype: str, kv_dtype: str, shard=None):
+    """Multi-token decode of one request ([P1] "Inapplicable scenarios and known
+    limitations" and [P4] "Future Roadmap": DCP combined with MTP / speculative
+    decoding; [P1] section 4: a token sees itself and earlier positions).
+
+    q: raw [T, Hq, D], the request's last T positions L-T .. L-1; k, v: raw
+    [L, Hkv, D], the whole sequence.  Token t attends positions 0 .. L-T+t
+    (and, with ``shard=(N, I, r)``, only those rank r owns).  Returns
+    (out [T, Hq, D], lse [T, Hq]) in fp64; a token with no visible key gets
+    zeros and -inf.
+    """
+    T = q.shape[0]
+    assert 1 <= T <= L
+    key_end = np.arange(L - T + 1, L + 1, dtype=np.int64)
+    return attention(q, k, v, key_begin=0, key_end=key_end, scale=scale, q_dtype=q_dtype,
+                     kv_dtype=kv_dtype, shard=shard)
+
+
 def lse_merge(part_out, part_lse):
     """Exact merge of partial attention results ([P3] Deep Dive 6).
 

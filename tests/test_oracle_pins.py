@@ -631,3 +631,56 @@ def test_a2a_pack_exchange_merge_gives_head_slices(N, Hq, Hkv):
     np.testing.assert_allclose(got, ro, rtol=2e-5, atol=2e-6)
     lse = np.concatenate([oracle.lse_merge_packed(recv[d], D)[1] for d in range(N)], axis=1)
     np.testing.assert_allclose(lse, rl, rtol=1e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# multi-token decode queries (speculative decoding / MTP)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,L,Hq,Hkv", [(2, 37, 8, 2), (4, 20, 4, 4), (3, 3, 2, 1), (1, 15, 4, 2)])
+def test_decode_mtp_is_the_last_rows_of_causal_sdpa(T, L, Hq, Hkv):
+    """Token t of the last T positions sees positions <= L - T + t: the last T
+    rows of torch's fp64 causal attention over the whole sequence."""
+    rng = np.random.default_rng(100 * T + L)
+    D = 8
+    q = rng.standard_normal((T, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    out, lse = oracle.decode_mtp(q, k, v, L=L, scale=0.4, q_dtype="f32", kv_dtype="f32")
+    # full causal attention of L queries, of which the last T are ours
+    qa = np.concatenate([rng.standard_normal((L - T, Hq, D)).astype(np.float32), q])
+    mask = torch.tril(torch.ones(L, L, dtype=torch.bool))
+    ro, rl = _sdpa(torch.from_numpy(qa).double().permute(1, 0, 2),
+                   torch.from_numpy(k).double().permute(1, 0, 2),
+                   torch.from_numpy(v).double().permute(1, 0, 2), 0.4, mask)
+    np.testing.assert_allclose(out, ro.permute(1, 0, 2).numpy()[L - T:], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, rl.permute(1, 0).numpy()[L - T:], rtol=1e-12, atol=1e-13)
+    if T == 1:  # one token is plain decode over the whole context
+        o1, l1 = oracle.attention(q, k, v, key_begin=0, key_end=L, scale=0.4, q_dtype="f32",
+                                  kv_dtype="f32")
+        assert np.array_equal(o1, out) and np.array_equal(l1, lse)
+
+
+@pytest.mark.parametrize("N,I,T,L", [(4, 4, 2, 50), (8, 16, 4, 70), (3, 1, 3, 10), (4, 8, 2, 9)])
+def test_merge_of_mtp_shard_partials_is_causal_attention(N, I, T, L):
+    """Each shard's partial of the T tokens (keys it owns, positions <= the
+    token's) merges exactly into the unsharded causal result; a token whose
+    shard owns no visible key has o = 0 and LSE -inf there."""
+    rng = np.random.default_rng(N * 1000 + L)
+    Hq, Hkv, D = 4, 2, 8
+    q = rng.standard_normal((T, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((L, Hkv, D)).astype(np.float32)
+    ro, rl = oracle.decode_mtp(q, k, v, L=L, scale=0.3, q_dtype="f32", kv_dtype="f32")
+    parts = [oracle.decode_mtp(q, k, v, L=L, scale=0.3, q_dtype="f32", kv_dtype="f32",
+                               shard=(N, I, r)) for r in range(N)]
+    po = np.stack([p[0] for p in parts])
+    pl = np.stack([p[1] for p in parts])
+    mo, ml = oracle.lse_merge(po.reshape(N, T * Hq, D), pl.reshape(N, T * Hq))
+    np.testing.assert_allclose(mo.reshape(T, Hq, D), ro, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ml.reshape(T, Hq), rl, rtol=1e-12, atol=1e-13)
+    for r in range(N):
+        for t in range(T):
+            visible = [p for p in range(L - T + t + 1) if oracle.owner(p, N, I) == r]
+            if not visible:
+                assert np.all(parts[r][0][t] == 0) and np.all(np.isneginf(parts[r][1][t]))
