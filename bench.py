@@ -92,28 +92,33 @@ class GqaDecodeBench:
         import kv_context_parallelism_amd as cp
 
         self.w, self.dev, self.cp, self.torch = w, dev, cp, torch
+        T = self.T = w.q_len  # query tokens per request: its last T positions
         seq = ci.uniform_lengths(w.B, w.ctx[0], w.ctx[1], w.seed)
         self.seq = seq
         offs = np.concatenate([[0], np.cumsum(seq)]).astype(np.int64)
         total = int(offs[-1])
-        self.q = ci.to_storage(ci.normal((w.B, w.Hq, w.D), w.seed + 1, dev), w.q_dtype)
+        qshape = (w.B, w.Hq, w.D) if T == 1 else (w.B, T, w.Hq, w.D)
+        self.q = ci.to_storage(ci.normal(qshape, w.seed + 1, dev), w.q_dtype)
         self.k = ci.to_storage(ci.normal((total, w.Hkv, w.D), w.seed + 2, dev), w.kv_dtype)
         self.v = ci.to_storage(ci.normal((total, w.Hkv, w.D), w.seed + 3, dev), w.kv_dtype)
         self.offs = offs
         seq_d = torch.from_numpy(seq).to(dev)
-        # context written before the step: every position but each request's last
-        req_ctx = torch.from_numpy(np.repeat(np.arange(w.B, dtype=np.int32), seq - 1)).to(dev)
-        pos_ctx = torch.from_numpy(np.concatenate([np.arange(L - 1, dtype=np.int32)
+        self.seq_d = seq_d
+        # context written before the step: every position but each request's last T
+        req_ctx = torch.from_numpy(np.repeat(np.arange(w.B, dtype=np.int32), seq - T)).to(dev)
+        pos_ctx = torch.from_numpy(np.concatenate([np.arange(L - T, dtype=np.int32)
                                                    for L in seq])).to(dev)
+        new_rows = (offs[1:, None] - T + np.arange(T)[None, :]).reshape(-1)
         keep = torch.ones(total, dtype=torch.bool, device=dev)
-        keep[torch.from_numpy(offs[1:] - 1).to(dev)] = False
+        keep[torch.from_numpy(new_rows).to(dev)] = False
         k_ctx, v_ctx = self.k[keep].contiguous(), self.v[keep].contiguous()
-        # the step's new tokens: position L_b - 1 of every request
-        last = torch.from_numpy(offs[1:] - 1).to(dev)
+        # the step's new tokens: positions L_b - T .. L_b - 1 of every request
+        last = torch.from_numpy(new_rows).to(dev)
         self.k_new = self.k[last].contiguous()
         self.v_new = self.v[last].contiguous()
-        self.req_new = torch.arange(w.B, dtype=torch.int32, device=dev)
-        self.pos_new = torch.from_numpy(seq - 1).to(dev)
+        self.req_new = torch.from_numpy(np.repeat(np.arange(w.B, dtype=np.int32), T)).to(dev)
+        self.pos_new = torch.from_numpy((seq[:, None] - T + np.arange(T)[None, :])
+                                        .reshape(-1).astype(np.int32)).to(dev)
         self.shards = []
         for r in range(w.N):
             ll_d = cp.cp_local_seq_lens(seq_d, r, w.N, w.I)
@@ -127,18 +132,24 @@ class GqaDecodeBench:
             ci.nan_fill_(vc, w.kv_dtype)
             slots = cp.cp_slot_map(req_ctx, pos_ctx, bt_d, r, w.N, w.I, w.bs)
             cp.cp_cache_write(slots, k_ctx, v_ctx, kc, vc, w.bs)
-            out = torch.empty(w.B, w.Hq, w.D, dtype=torch.float32, device=dev)
-            lse = torch.empty(w.B, w.Hq, dtype=torch.float32, device=dev)
-            args = cp.gqa_args(self.q, kc, vc, bt_d, ll_d, w.scale, out, lse)
-            ws = torch.empty(max(cp.cp_workspace_bytes(cp.CP_OP_DECODE_GQA, args), 16),
-                             dtype=torch.uint8, device=dev)
+            out = torch.empty(qshape, dtype=torch.float32, device=dev)
+            lse = torch.empty(qshape[:-1], dtype=torch.float32, device=dev)
+            if T == 1:
+                args, op = cp.gqa_args(self.q, kc, vc, bt_d, ll_d, w.scale, out, lse), \
+                    cp.CP_OP_DECODE_GQA
+            else:
+                args = cp.gqa_mtp_args(self.q, kc, vc, bt_d, ll_d, seq_d, w.scale, out, lse, r,
+                                       w.N, w.I)
+                op = cp.CP_OP_DECODE_GQA_MTP
+            ws = torch.empty(max(cp.cp_workspace_bytes(op, args), 16), dtype=torch.uint8,
+                             device=dev)
             self.shards.append(dict(ll=ll, ll_d=ll_d, bt_d=bt_d, kc=kc, vc=vc, ws=ws,
-                                    slots=torch.empty(w.B, dtype=torch.int64, device=dev)))
+                                    slots=torch.empty(w.B * T, dtype=torch.int64, device=dev)))
         del k_ctx, v_ctx, req_ctx, pos_ctx, keep
-        self.part_out = torch.empty(w.N, w.B, w.Hq, w.D, dtype=torch.float32, device=dev)
-        self.part_lse = torch.empty(w.N, w.B, w.Hq, dtype=torch.float32, device=dev)
-        self.out = torch.empty(w.B, w.Hq, w.D, dtype=torch.float32, device=dev)
-        self.lse = torch.empty(w.B, w.Hq, dtype=torch.float32, device=dev)
+        self.part_out = torch.empty((w.N,) + qshape, dtype=torch.float32, device=dev)
+        self.part_lse = torch.empty((w.N,) + qshape[:-1], dtype=torch.float32, device=dev)
+        self.out = torch.empty(qshape, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(qshape[:-1], dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
         kv_tok = w.Hkv * w.D * self.q.element_size() * 2
         self.kv_bytes_step = int(seq.sum()) * kv_tok
@@ -146,12 +157,14 @@ class GqaDecodeBench:
         for sh in self.shards:
             self.per_launch_bytes.append(int(sh["ll"].sum()) * kv_tok
                                          + self.q.numel() * self.q.element_size()
-                                         + w.B * w.Hq * (w.D + 1) * 4)
+                                         + w.B * T * w.Hq * (w.D + 1) * 4)
         self.work_step = self.kv_bytes_step
         self.per_launch_work = self.per_launch_bytes
         self.launches_per_step = w.N
         self.dominant = list(range(w.N))
-        self.kernel_name = "cp_decode_attn_partial_gqa (attention + split combine)"
+        self.kernel_name = ("cp_decode_attn_partial_gqa (attention + split combine)" if T == 1 else
+                            f"cp_decode_attn_partial_gqa_mtp ({T} query tokens; attention + split "
+                            "combine)")
         self.dtype = w.kv_dtype
 
     def step(self, ev=None):
@@ -163,9 +176,15 @@ class GqaDecodeBench:
         for r, sh in enumerate(self.shards):
             if ev is not None:
                 ev[r][0].record()
-            cp.cp_decode_attn_partial_gqa(self.q, sh["kc"], sh["vc"], sh["bt_d"], sh["ll_d"],
-                                          w.scale, out=self.part_out[r], lse=self.part_lse[r],
-                                          workspace=sh["ws"])
+            if self.T == 1:
+                cp.cp_decode_attn_partial_gqa(self.q, sh["kc"], sh["vc"], sh["bt_d"], sh["ll_d"],
+                                              w.scale, out=self.part_out[r], lse=self.part_lse[r],
+                                              workspace=sh["ws"])
+            else:
+                cp.cp_decode_attn_partial_gqa_mtp(self.q, sh["kc"], sh["vc"], sh["bt_d"],
+                                                  sh["ll_d"], self.seq_d, w.scale, r, w.N, w.I,
+                                                  out=self.part_out[r], lse=self.part_lse[r],
+                                                  workspace=sh["ws"])
             if ev is not None:
                 ev[r][1].record()
         cp.cp_lse_merge(self.part_out, self.part_lse, out=self.out, lse_out=self.lse)
@@ -188,11 +207,16 @@ class GqaDecodeBench:
             v = ci.bits(self.v[lo:hi].cpu())
             po, pl = [], []
             for r in range(w.N):
-                o, l = oracle.attention(q[b:b + 1], k, v, key_begin=0, key_end=hi - lo,
-                                        scale=w.scale, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
-                                        shard=(w.N, w.I, r))
-                po.append(o[0])
-                pl.append(l[0])
+                if self.T == 1:
+                    o, l = oracle.attention(q[b:b + 1], k, v, key_begin=0, key_end=hi - lo,
+                                            scale=w.scale, q_dtype=w.q_dtype,
+                                            kv_dtype=w.kv_dtype, shard=(w.N, w.I, r))
+                else:
+                    o, l = oracle.decode_mtp(q[b], k, v, L=hi - lo, scale=w.scale,
+                                             q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
+                                             shard=(w.N, w.I, r))
+                po.append(o.reshape(-1, w.D))
+                pl.append(l.reshape(-1))
             oracle.lse_merge(np.stack(po), np.stack(pl))
             done += 1
             kv_bytes += (hi - lo) * w.Hkv * w.D * 2 * 2
@@ -206,7 +230,7 @@ class GqaDecodeBench:
         return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
                 "head_dim": w.D, "context": f"uniform[{w.ctx[0]},{w.ctx[1]}]",
                 "total_context_tokens": int(self.seq.sum()), "dcp_shards": w.N,
-                "interleave": w.I, "block_size": w.bs}
+                "interleave": w.I, "block_size": w.bs, "query_tokens": self.T}
 
 
 
@@ -761,8 +785,8 @@ class HeadScatterBench:
 BENCHES = {"gqa_decode": GqaDecodeBench, "mla_decode": MlaDecodeBench,
            "pcp_prefill": PrefillBench, "dcp_prefill": DcpPrefillBench,
            "kv_gather": KvGatherBench, "head_scatter": HeadScatterBench}
-BENCH_WORKLOADS = ["gqa_decode_bf16", "mla_decode_bf16", "mla_decode_fp8", "pcp_prefill_bf16",
-                   "dcp_prefill_bf16", "kv_gather_bf16", "head_scatter_mla"]
+BENCH_WORKLOADS = ["gqa_decode_bf16", "gqa_decode_mtp_bf16", "mla_decode_bf16", "mla_decode_fp8",
+                   "pcp_prefill_bf16", "dcp_prefill_bf16", "kv_gather_bf16", "head_scatter_mla"]
 
 
 def main():

@@ -57,6 +57,7 @@ class Workload:
     C: int = 0                     # prefill: new-chunk length
     P: int = 0                     # prefill: cached-prefix length
     seed: int = 1000
+    q_len: int = 1                 # decode: query tokens per request (the last q_len positions)
     extra: dict = field(default_factory=dict)
 
 
@@ -69,6 +70,11 @@ WORKLOADS = {
     "gqa_decode_bf16": Workload("gqa_decode_bf16", "gqa_decode", B=32, Hq=32, Hkv=8, D=128,
                                 Dv=128, ctx=(4096, 32768), N=8, I=16, bs=16, q_dtype="bf16",
                                 kv_dtype="bf16", scale=1 / math.sqrt(128), seed=1002),
+    # the same decode step with two query tokens per request (one speculative
+    # token verified with the current one), causal on the interleaved positions
+    "gqa_decode_mtp_bf16": Workload("gqa_decode_mtp_bf16", "gqa_decode", B=32, Hq=32, Hkv=8, D=128,
+                                Dv=128, ctx=(4096, 32768), N=8, I=16, bs=16, q_dtype="bf16",
+                                kv_dtype="bf16", scale=1 / math.sqrt(128), seed=1009, q_len=2),
     # absorbed MLA decode, bf16 latent 576 (512 + 64 rope), value width 512
     "mla_decode_bf16": Workload("mla_decode_bf16", "mla_decode", B=64, Hq=128, Hkv=1, D=576,
                                 Dv=512, ctx=(65536, 65536), N=8, I=1, bs=64, q_dtype="bf16",

@@ -145,6 +145,38 @@ typedef struct cp_gqa_args {
 cp_status cp_decode_attn_partial_gqa(const cp_gqa_args *args, void *workspace,
                                      size_t workspace_bytes, hipStream_t stream);
 
+/* Multi-token decode queries (speculative decoding / MTP verification: [P1]
+ * "Inapplicable scenarios and known limitations" and [P4] "Future Roadmap"
+ * name the combination of DCP with MTP and speculative decoding).  Request b's
+ * q_len query tokens are its last q_len positions, seq_len[b] - q_len + t for
+ * t = 0 .. q_len-1, their K/V already written to the caches; token t attends
+ * the keys at positions <= its own ("a token sees itself and earlier
+ * positions", [P1] section 4).  On DCP rank dcp_rank of dcp_size (interleave
+ * I) the shard holds local keys in increasing position order, so token t sees
+ * the shard's first min(local_len[b], owned_below(seq_len[b] - q_len + t + 1))
+ * keys, owned_below(x) = floor(x / (N I)) I + clamp(x mod N I - rank I, 0, I)
+ * ([P1] section 2).  A token with no visible key on the shard gets o = 0 and
+ * LSE -inf.
+ *   base.q   [B][q_len][Hq][D], base.out [B][q_len][Hq][D] fp32,
+ *   base.lse [B][q_len][Hq] fp32; other base fields as cp_gqa_args.
+ * Supported: 256-byte K/V rows (bf16 D 128 or fp32 D 64) with
+ * q_len * Hq/Hkv in {1, 2, 4, 8}.  seq_len[b] < q_len gives NaN rows.
+ * Workspace: cp_workspace_bytes(CP_OP_DECODE_GQA_MTP, &args); need not be
+ * initialised.
+ * Errors: as cp_decode_attn_partial_gqa, plus CP_E_INVALID for q_len < 1, a
+ * rank outside [0, dcp_size), interleave < 1, NULL seq_len; CP_E_UNSUPPORTED
+ * for other shapes. */
+typedef struct cp_gqa_mtp_args {
+    cp_gqa_args base;
+    int32_t q_len;              /* query tokens per request */
+    int32_t dcp_rank, dcp_size; /* this shard's rank and the DCP group size */
+    int32_t interleave;         /* I: consecutive positions per rank */
+    const int32_t *seq_len;     /* [B] global context length, including the q_len tokens */
+} cp_gqa_mtp_args;
+
+cp_status cp_decode_attn_partial_gqa_mtp(const cp_gqa_mtp_args *args, void *workspace,
+                                         size_t workspace_bytes, hipStream_t stream);
+
 typedef struct cp_mla_args {
     const void *q;              /* [B][H][Dk] bf16 absorbed queries */
     const void *kv_cache;       /* [num_blocks][bs][Dk], dtype kv_dt: latent rows */
@@ -343,6 +375,7 @@ cp_status cp_kv_gather(const cp_kv_gather_args *args, hipStream_t stream);
 #define CP_OP_DECODE_GQA 1
 #define CP_OP_DECODE_MLA 2
 #define CP_OP_PREFILL 3
+#define CP_OP_DECODE_GQA_MTP 4
 
 /* Bytes of device workspace the call with these arguments needs (0 if none);
  * args points to the op's argument struct.  Returns (size_t)-1 for an unknown

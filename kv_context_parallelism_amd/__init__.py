@@ -17,11 +17,12 @@ import torch
 from . import _lib
 from ._lib import (CP_BF16, CP_E_HIP, CP_E_INVALID, CP_E_UNSUPPORTED, CP_E_WORKSPACE, CP_F32,
                    CP_FP8_E4M3FN, CP_KV_DENSE, CP_KV_PAGED, CP_KV_PAGED_CAUSAL, CP_OK,
-                   CP_OP_DECODE_GQA,
+                   CP_OP_DECODE_GQA, CP_OP_DECODE_GQA_MTP,
                    CP_OP_DECODE_MLA, CP_OP_PREFILL, CP_SLOT_INVALID, CP_SLOT_NOT_MINE, CP_MAX_SHARDS)
 
 __all__ = [
     "CpError", "cp_local_seq_lens", "cp_slot_map", "cp_cache_write", "cp_decode_attn_partial_gqa",
+    "cp_decode_attn_partial_gqa_mtp", "gqa_mtp_args",
     "cp_decode_attn_partial_mla", "cp_lse_merge", "cp_lse_correct", "cp_a2a_pack",
     "cp_lse_merge_packed", "pcp_prefill_attn_causal", "cp_workspace_bytes",
     "gqa_args", "mla_args", "prefill_args", "library_path", "cp_kv_gather", "kv_gather_args",
@@ -182,6 +183,43 @@ def cp_decode_attn_partial_gqa(q, k_cache, v_cache, block_table, local_len, scal
     ws, nws = _workspace(CP_OP_DECODE_GQA, a, q.device, workspace)
     _check(lib.cp_decode_attn_partial_gqa(ctypes.byref(a), _ptr(ws), nws, _stream(stream)),
            "cp_decode_attn_partial_gqa")
+    return out, lse
+
+
+def gqa_mtp_args(q, k_cache, v_cache, block_table, local_len, seq_len, scale, out, lse, rank, N,
+                 I):
+    """Arguments of the multi-token entry; q [B][T][Hq][D], out [B][T][Hq][D],
+    lse [B][T][Hq]."""
+    B, T, Hq, D = q.shape
+    nb, Hkv, bs, D2 = k_cache.shape
+    if D2 != D or v_cache.shape != k_cache.shape:
+        raise ValueError("cache shape mismatch")
+    base = _lib.CpGqaArgs(q=_ptr(q), k_cache=_ptr(k_cache), v_cache=_ptr(v_cache),
+                          block_table=_i32(block_table, "block_table"),
+                          local_len=_i32(local_len, "local_len"), B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs,
+                          bt_stride=block_table.shape[1], num_blocks=nb, scale=scale, dt=_dt(q),
+                          out=_ptr(out), lse=_ptr(lse))
+    return _lib.CpGqaMtpArgs(base=base, q_len=T, dcp_rank=int(rank), dcp_size=int(N),
+                             interleave=int(I), seq_len=_i32(seq_len, "seq_len"))
+
+
+def cp_decode_attn_partial_gqa_mtp(q, k_cache, v_cache, block_table, local_len, seq_len, scale,
+                                   rank, N, I, out=None, lse=None, workspace=None, stream=None):
+    """Partial attention of T query tokens per request, q [B][T][Hq][D] (the
+    last T positions of each request, causal on the shard's interleaved
+    positions), over one shard's paged KV; returns (out fp32 [B][T][Hq][D],
+    lse fp32 [B][T][Hq])."""
+    lib = _lib.load()
+    B, T, Hq, D = q.shape
+    if out is None:
+        out = torch.empty(B, T, Hq, D, dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty(B, T, Hq, dtype=torch.float32, device=q.device)
+    a = gqa_mtp_args(q, k_cache, v_cache, block_table, local_len, seq_len, scale, out, lse, rank,
+                     N, I)
+    ws, nws = _workspace(CP_OP_DECODE_GQA_MTP, a, q.device, workspace)
+    _check(lib.cp_decode_attn_partial_gqa_mtp(ctypes.byref(a), _ptr(ws), nws, _stream(stream)),
+           "cp_decode_attn_partial_gqa_mtp")
     return out, lse
 
 

@@ -11,7 +11,7 @@ CP_OK, CP_E_INVALID, CP_E_UNSUPPORTED, CP_E_WORKSPACE, CP_E_HIP = range(5)
 CP_F32, CP_BF16, CP_FP8_E4M3FN = range(3)
 CP_SLOT_NOT_MINE, CP_SLOT_INVALID = -1, -2
 CP_KV_DENSE, CP_KV_PAGED, CP_KV_PAGED_CAUSAL = 0, 1, 2
-CP_OP_DECODE_GQA, CP_OP_DECODE_MLA, CP_OP_PREFILL = 1, 2, 3
+CP_OP_DECODE_GQA, CP_OP_DECODE_MLA, CP_OP_PREFILL, CP_OP_DECODE_GQA_MTP = 1, 2, 3, 4
 CP_MAX_SHARDS = 16
 
 _vp, _i32, _i64, _f32, _int = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
@@ -23,6 +23,11 @@ class CpGqaArgs(ctypes.Structure):
                 ("local_len", _vp), ("B", _i32), ("Hq", _i32), ("Hkv", _i32), ("D", _i32),
                 ("bs", _i32), ("bt_stride", _i32), ("num_blocks", _i64), ("scale", _f32),
                 ("dt", _int), ("out", _vp), ("lse", _vp)]
+
+
+class CpGqaMtpArgs(ctypes.Structure):
+    _fields_ = [("base", CpGqaArgs), ("q_len", _i32), ("dcp_rank", _i32), ("dcp_size", _i32),
+                ("interleave", _i32), ("seq_len", _vp)]
 
 
 class CpMlaArgs(ctypes.Structure):
@@ -58,6 +63,8 @@ SIGNATURES = {
                            _vp]),
     "cp_cache_write": (_int, [_i64, _vp, _vp, _vp, _i32, _i32, _int, _vp, _vp, _i64, _i32, _vp]),
     "cp_decode_attn_partial_gqa": (_int, [ctypes.POINTER(CpGqaArgs), _vp, ctypes.c_size_t, _vp]),
+    "cp_decode_attn_partial_gqa_mtp": (_int, [ctypes.POINTER(CpGqaMtpArgs), _vp, ctypes.c_size_t,
+                                              _vp]),
     "cp_decode_attn_partial_mla": (_int, [ctypes.POINTER(CpMlaArgs), _vp, ctypes.c_size_t, _vp]),
     "cp_lse_merge": (_int, [_i32, _i64, _i32, _vp, _vp, _vp, _int, _vp, _vp]),
     "cp_lse_correct": (_int, [_i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),

@@ -47,6 +47,8 @@ size_t cp_workspace_bytes(int op, const void *args) {
     if (!args) return (size_t)-1;
     switch (op) {
     case CP_OP_DECODE_GQA: return cpattn::plan_gqa(*static_cast<const cp_gqa_args *>(args)).ws_bytes;
+    case CP_OP_DECODE_GQA_MTP:
+        return cpattn::plan_gqa_mtp(*static_cast<const cp_gqa_mtp_args *>(args)).ws_bytes;
     case CP_OP_DECODE_MLA: return cpattn::plan_mla(*static_cast<const cp_mla_args *>(args)).ws_bytes;
     case CP_OP_PREFILL: return 0;
     }

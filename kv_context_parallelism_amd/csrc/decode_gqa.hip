@@ -402,18 +402,29 @@ int log2_exact(int32_t x) {
 
 }  // namespace
 
-GqaPlan plan_gqa(const cp_gqa_args &a) {
+// Row-layout kernel: one partial slot per launched wave plus one per
+// (request, KV head) boundary, then a (first, count) table.  T query tokens
+// per request give T x Hq/Hkv rows per KV head.
+static GqaPlan plan_rows(const cp_gqa_args &a, int T, bool mtp) {
     GqaPlan pl{};
-    if (gqa_rows_supported(a)) {
-        // row-layout kernel: one partial slot per launched wave plus one per
-        // (request, KV head) boundary, then a (first, count) table
-        const int G = a.Hq / a.Hkv;
-        pl.rows = true;
-        pl.waves = gqa_rows_waves(a);
-        const size_t slots = (size_t)pl.waves + (size_t)a.B * a.Hkv;
-        pl.ws_bytes = slots * G * (a.D + 1) * sizeof(float) + (size_t)a.B * a.Hkv * 2 * 4 + 512;
-        return pl;
-    }
+    const int G = a.Hq / a.Hkv * T;
+    pl.rows = true;
+    pl.waves = gqa_rows_waves(a, T, mtp);
+    const size_t slots = (size_t)pl.waves + (size_t)(a.B > 0 ? a.B : 0) * a.Hkv;
+    pl.ws_bytes = slots * G * (a.D + 1) * sizeof(float) + (size_t)(a.B > 0 ? a.B : 0) * a.Hkv * 2 * 4 + 512;
+    return pl;
+}
+
+GqaPlan plan_gqa_mtp(const cp_gqa_mtp_args &m) {
+    const cp_gqa_args &a = m.base;
+    if (a.Hkv < 1 || a.Hq % a.Hkv != 0 || m.q_len < 1 || !gqa_rows_supported(a, m.q_len))
+        return GqaPlan{};
+    return plan_rows(a, m.q_len, true);
+}
+
+GqaPlan plan_gqa(const cp_gqa_args &a) {
+    if (gqa_rows_supported(a)) return plan_rows(a, 1, false);
+    GqaPlan pl{};
     // General kernel: split the capacity of each (request, KV head) into work
     // items of S tokens so that about 8K items exist; the hardware dispatcher
     // then balances the tail at the granularity of one item.  S is a power of
@@ -434,10 +445,11 @@ GqaPlan plan_gqa(const cp_gqa_args &a) {
 
 using namespace cpattn;
 
-extern "C" cp_status cp_decode_attn_partial_gqa(const cp_gqa_args *a, void *ws, size_t ws_bytes,
-                                                hipStream_t stream) {
-    clear_error();
-    if (!a) return fail(CP_E_INVALID, "cp_decode_attn_partial_gqa: NULL args");
+namespace cpattn {
+namespace {
+
+// Host checks shared by the single- and multi-token entries (CP_OK or the error).
+cp_status validate_gqa(const cp_gqa_args *a) {
     if (a->B < 0 || a->Hq < 1 || a->Hkv < 1 || a->D < 1 || a->bs < 1 || a->bt_stride < 1 ||
         a->num_blocks < 0)
         return fail(CP_E_INVALID, "gqa decode: B=%d Hq=%d Hkv=%d D=%d bs=%d bt_stride=%d", a->B,
@@ -459,37 +471,89 @@ extern "C" cp_status cp_decode_attn_partial_gqa(const cp_gqa_args *a, void *ws, 
     if (!aligned16(a->q) || !aligned16(a->k_cache) || !aligned16(a->v_cache) ||
         !aligned16(a->out))
         return fail(CP_E_INVALID, "gqa decode: q, caches and out must be 16-byte aligned");
+    return CP_OK;
+}
+
+// The row-layout kernel and its split combine: T x Hq/Hkv rows per KV head,
+// merged into out [B][T][Hq][D] and lse [B][T][Hq].
+cp_status run_rows(const cp_gqa_args *a, int bs_log2, void *ws, const GqaPlan &pl,
+                   const GqaMtp &mtp, hipStream_t stream) {
+    const int T = mtp.T;
+    const int G = a->Hq / a->Hkv * T;
+    const size_t slots = (size_t)pl.waves + (size_t)a->B * a->Hkv;
+    float *ws_o = static_cast<float *>(ws);
+    float *ws_l = ws_o + slots * G * a->D;
+    int32_t *seg = reinterpret_cast<int32_t *>(
+        (reinterpret_cast<uintptr_t>(ws_l + slots * G) + 255) & ~uintptr_t(255));
+    cp_status st = gqa_rows_launch(*a, bs_log2, ws_o, ws_l, seg, pl.waves, mtp, stream);
+    if (st != CP_OK) return st;
+    MergeDesc m;
+    m.seg = seg;
+    m.rows_per_seg = G;
+    m.n_parts = 0;
+    m.rows = (int64_t)a->B * a->Hq * T;
+    m.Dv = a->D;
+    m.part_out = ws_o;
+    m.part_lse = ws_l;
+    m.o_part_stride = (int64_t)G * a->D;
+    m.o_row_stride = a->D;
+    m.l_part_stride = G;
+    m.l_row_stride = 1;
+    m.out = a->out;
+    m.out_dt = CP_F32;
+    m.lse_out = a->lse;
+    m.remap_T = T;
+    m.remap_G = a->Hq / a->Hkv;
+    m.remap_Hkv = a->Hkv;
+    return launch_merge(m, stream);
+}
+
+}  // namespace
+}  // namespace cpattn
+
+extern "C" cp_status cp_decode_attn_partial_gqa_mtp(const cp_gqa_mtp_args *m, void *ws,
+                                                    size_t ws_bytes, hipStream_t stream) {
+    clear_error();
+    if (!m) return fail(CP_E_INVALID, "cp_decode_attn_partial_gqa_mtp: NULL args");
+    const cp_gqa_args *a = &m->base;
+    cp_status st = validate_gqa(a);
+    if (st != CP_OK || a->B == 0) return st;
+    if (m->q_len < 1 || m->dcp_size < 1 || m->dcp_rank < 0 || m->dcp_rank >= m->dcp_size ||
+        m->interleave < 1 || (int64_t)m->dcp_size * m->interleave > (1 << 30))
+        return fail(CP_E_INVALID, "gqa mtp decode: q_len=%d dcp rank %d of %d, interleave %d",
+                    m->q_len, m->dcp_rank, m->dcp_size, m->interleave);
+    if (!m->seq_len) return fail(CP_E_INVALID, "gqa mtp decode: NULL seq_len");
+    if (!gqa_rows_supported(*a, m->q_len))
+        return fail(CP_E_UNSUPPORTED,
+                    "gqa mtp decode: q_len x Hq/Hkv = %d (the row kernel takes 1, 2, 4 or 8 rows "
+                    "per KV head of 256-byte K/V rows)",
+                    m->q_len * (a->Hq / a->Hkv));
+    const GqaPlan pl = plan_gqa_mtp(*m);
+    if (!ws || ws_bytes < pl.ws_bytes)
+        return fail(CP_E_WORKSPACE, "gqa mtp decode: workspace of %zu bytes needed, %zu given",
+                    pl.ws_bytes, ws_bytes);
+    GqaMtp mtp;
+    mtp.T = m->q_len;
+    mtp.seq_len = m->seq_len;
+    mtp.dcp_rank = m->dcp_rank;
+    mtp.dcp_size = m->dcp_size;
+    mtp.dcp_I = m->interleave;
+    return run_rows(a, log2_exact(a->bs), ws, pl, mtp, stream);
+}
+
+extern "C" cp_status cp_decode_attn_partial_gqa(const cp_gqa_args *a, void *ws, size_t ws_bytes,
+                                                hipStream_t stream) {
+    clear_error();
+    if (!a) return fail(CP_E_INVALID, "cp_decode_attn_partial_gqa: NULL args");
+    cp_status st0 = validate_gqa(a);
+    if (st0 != CP_OK || a->B == 0) return st0;
+    const int bs_log2 = log2_exact(a->bs);
     const GqaPlan pl = plan_gqa(*a);
     if (pl.ws_bytes > 0 && (!ws || ws_bytes < pl.ws_bytes))
         return fail(CP_E_WORKSPACE, "gqa decode: workspace of %zu bytes needed, %zu given",
                     pl.ws_bytes, ws_bytes);
 
-    if (pl.rows) {
-        const int G = a->Hq / a->Hkv;
-        const size_t slots = (size_t)pl.waves + (size_t)a->B * a->Hkv;
-        float *ws_o = static_cast<float *>(ws);
-        float *ws_l = ws_o + slots * G * a->D;
-        int32_t *seg = reinterpret_cast<int32_t *>(
-            (reinterpret_cast<uintptr_t>(ws_l + slots * G) + 255) & ~uintptr_t(255));
-        cp_status st = gqa_rows_launch(*a, bs_log2, ws_o, ws_l, seg, pl.waves, stream);
-        if (st != CP_OK) return st;
-        MergeDesc m;
-        m.seg = seg;
-        m.rows_per_seg = G;
-        m.n_parts = 0;
-        m.rows = (int64_t)a->B * a->Hq;
-        m.Dv = a->D;
-        m.part_out = ws_o;
-        m.part_lse = ws_l;
-        m.o_part_stride = (int64_t)G * a->D;
-        m.o_row_stride = a->D;
-        m.l_part_stride = G;
-        m.l_row_stride = 1;
-        m.out = a->out;
-        m.out_dt = CP_F32;
-        m.lse_out = a->lse;
-        return launch_merge(m, stream);
-    }
+    if (pl.rows) return run_rows(a, bs_log2, ws, pl, GqaMtp{}, stream);
 
     GqaParams p;
     p.q = to_global(a->q);

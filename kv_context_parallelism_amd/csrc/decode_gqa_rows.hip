@@ -56,7 +56,27 @@ struct RowParams {
     float *ws_o;      // [slots][G][D]
     float *ws_l;      // [slots][G]
     int32_t *seg;     // [B*Hkv][2]: first slot, count
+    // Multi-token queries: the kernel's G = T x Greal rows per KV head are
+    // query token t (the request's position seq_len - T + t) of head
+    // g Greal + h, row t Greal + h.  Token t sees the shard's keys at
+    // positions <= its own (seq_len == nullptr: T = 1, no limit).
+    const int32_t *seq_len;
+    int32_t T, Greal;
+    int32_t dcp_rank, dcp_size, dcp_I;
 };
+
+// Positions below x held by DCP rank r of N with interleave I ("Breaking the
+// Long-Sequence Inference Bottleneck ...", section 2: the owner of position t
+// is floor(t / I) mod N): whole rounds of N I positions give I each, the
+// partial round the overlap of [0, x mod N I) with [r I, r I + I).  A shard's
+// local keys are its positions in increasing order, so this is also the
+// number of local keys a query at position x - 1 may see.
+__device__ __forceinline__ int32_t owned_below(int32_t x, int32_t r, int32_t N, int32_t I) {
+    if (x <= 0) return 0;
+    const int32_t round = N * I;
+    const int32_t q = x / round, rem = x - q * round;
+    return q * I + min(max(rem - r * I, 0), I);
+}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -132,7 +152,7 @@ __device__ __forceinline__ int64_t owner_of(int64_t c, int64_t R, int64_t W) {
     return ((c + 1) * W - 1) / R;
 }
 
-template <int EB, int G, int MINWG>
+template <int EB, int G, int MINWG, bool kMtp>
 __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams p) {
     constexpr bool kBf16 = (EB == 2);
     constexpr int D = 256 / EB;                 // 128 bf16 or 64 fp32
@@ -239,8 +259,25 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
         const int32_t s0 = k * kTile;
         const int32_t s1 = min(s0 + nseg * kTile, L);
         const int64_t slot = w + (int64_t)b * p.Hkv + g;
-        const int h0 = g * G;
         cint32 *bt_row = p.bt + (int64_t)b * p.bt_stride;
+        // Key limits: row hh (query token hh / Greal) sees local keys below
+        // lim[k2] of this piece; min_lim is the first token's, the smallest.
+        int32_t qpos0 = 0;  // position of query token 0
+        if constexpr (kMtp) {
+            qpos0 = p.seq_len[b] - p.T;
+            bad |= qpos0 < 0;
+        }
+        auto causal_lim = [&](int t) -> int32_t {
+            if constexpr (!kMtp) return s1;
+            return min(s1, owned_below(qpos0 + t + 1, p.dcp_rank, p.dcp_size, p.dcp_I));
+        };
+        const int32_t min_lim = causal_lim(0);
+        int32_t lim[NF];
+#pragma unroll
+        for (int k2 = 0; k2 < NF; ++k2) {
+            const int hh = NV >= 16 ? qp * NF + k2 : (qp / REP) % G;
+            lim[k2] = causal_lim(hh / p.Greal);
+        }
 
         // First cache row (head g) of the 16-token group at local index lb.  The
         // block id is a uniform (scalar) load, so waiting for it never waits for
@@ -292,8 +329,10 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
         }
         u32x4 qraw[G];
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh)
-            qraw[hh] = load16(p.q + ((int64_t)b * p.Hq + h0 + hh) * 256 + c * 16);
+        for (int hh = 0; hh < G; ++hh) {
+            const int t = hh / p.Greal, h = hh - t * p.Greal;
+            qraw[hh] = load16(p.q + (((int64_t)b * p.T + t) * p.Hq + g * p.Greal + h) * 256 + c * 16);
+        }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         float qf[kBf16 ? 1 : G][4];
         if constexpr (!kBf16) {
@@ -309,6 +348,8 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
         auto tile = [&](int32_t tb, auto tail_tag) {
             constexpr bool kTail = decltype(tail_tag)::value;
             const int32_t tn = tb + kTile;
+            // keys of this tile past some row's limit (multi-token queries)
+            const bool mask = kTail || (kMtp && tn > min_lim);
             // Block ids of the next tile, early: they are needed after the scores.
             // Full tiles always prefetch (past the segment's end the rows clamp to
             // the current tile and the reads hit the cache): a conditional
@@ -340,10 +381,12 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
                     }
                 row_reduce_scatter<NV>(v, c);
                 // this lane's scores belong to token (c >> 2) of its row
-                const bool ok = !kTail || (tb + gi * 16 + (c >> 2) * 4 + R) < s1;
+                const int32_t tok = tb + gi * 16 + (c >> 2) * 4 + R;
 #pragma unroll
-                for (int k2 = 0; k2 < NF; ++k2)
+                for (int k2 = 0; k2 < NF; ++k2) {
+                    const bool ok = !mask || tok < lim[k2];
                     sc[gi][k2] = ok ? (kBf16 ? v[k2] * p.qk_scale : v[k2]) : -INFINITY;
+                }
             }
             if constexpr (!kTail) load_tile(p.kc, rows_next, kreg);
 
@@ -359,12 +402,15 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
                 mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
                 mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
                 const float mn = fmaxf(m[k2], mt);
-                alpha[k2] = fast_exp2(m[k2] - mn);
+                // a row with no visible key yet (multi-token queries) keeps
+                // m = -inf: no rescale, and its masked scores give 0
+                const float mref = kMtp && mn == -INFINITY ? 0.f : mn;
+                alpha[k2] = kMtp && mn == -INFINITY ? 1.f : fast_exp2(m[k2] - mn);
                 m[k2] = mn;
                 float ps = 0.f;
 #pragma unroll
                 for (int gi = 0; gi < kNG; ++gi) {
-                    sc[gi][k2] = fast_exp2(sc[gi][k2] - mn);
+                    sc[gi][k2] = fast_exp2(sc[gi][k2] - mref);
                     ps += sc[gi][k2];
                 }
                 lpart[k2] = lpart[k2] * alpha[k2] + ps;
@@ -507,7 +553,8 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
                                       : (q == 2 ? quad_bcast<2>(lsum[0]) : quad_bcast<3>(lsum[0])));
             }
             if (R == 0) {
-                const float inv = bad ? NAN : (empty ? 0.f : 1.f / lh);
+                // a row without any visible key of this piece: 0 and LSE -inf
+                const float inv = bad ? NAN : (empty || !(lh > 0.f) ? 0.f : 1.f / lh);
                 float *dst = o_dst + hh * D + c * EPC;
 #pragma unroll
                 for (int e = 0; e < EPC; e += 4)
@@ -520,7 +567,9 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
 #pragma unroll
             for (int k2 = 0; k2 < NF; ++k2) {
                 const int hh = NV >= 16 ? c * NF + k2 : c / REP;
-                l_dst[hh] = bad ? NAN : (empty ? -INFINITY : (m[k2] + fast_log2(lsum[k2])) * kLn2);
+                l_dst[hh] = bad ? NAN
+                                : (empty || !(lsum[k2] > 0.f) ? -INFINITY
+                                                              : (m[k2] + fast_log2(lsum[k2])) * kLn2);
             }
         }
         cc += nseg;
@@ -530,20 +579,24 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
 template <int EB, int G>
 cp_status launch_rows(const RowParams &p, hipStream_t stream) {
     const int64_t blocks = ceil_div(p.W, kWaves);
-    hipLaunchKernelGGL((gqa_rows_kernel<EB, G, kMinWgPerCu>), dim3((unsigned)blocks), dim3(64 * kWaves), 0,
-                       stream, p);
+    if (p.seq_len)
+        hipLaunchKernelGGL((gqa_rows_kernel<EB, G, kMinWgPerCu, true>), dim3((unsigned)blocks),
+                           dim3(64 * kWaves), 0, stream, p);
+    else
+        hipLaunchKernelGGL((gqa_rows_kernel<EB, G, kMinWgPerCu, false>), dim3((unsigned)blocks),
+                           dim3(64 * kWaves), 0, stream, p);
     return check_launch("cp_decode_attn_partial_gqa");
 }
 
 }  // namespace
 
-bool gqa_rows_supported(const cp_gqa_args &a) {
-    const int G = a.Hkv > 0 ? a.Hq / a.Hkv : 0;
+bool gqa_rows_supported(const cp_gqa_args &a, int T) {
+    const int G = a.Hkv > 0 ? a.Hq / a.Hkv * T : 0;
     const bool row256 = (a.dt == CP_BF16 && a.D == 128) || (a.dt == CP_F32 && a.D == 64);
     return row256 && (G == 1 || G == 2 || G == 4 || G == 8) && a.B <= kMaxB;
 }
 
-template <int EB, int G>
+template <int EB, int G, bool kMtp>
 int resident_wgs() {
     static int cached[64] = {0};
     int dev = 0;
@@ -551,7 +604,7 @@ int resident_wgs() {
     if (cached[dev] == 0) {
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &n, reinterpret_cast<const void *>(gqa_rows_kernel<EB, G, kMinWgPerCu>),
+                &n, reinterpret_cast<const void *>(gqa_rows_kernel<EB, G, kMinWgPerCu, kMtp>),
                 64 * kWaves, 0) != hipSuccess ||
             n < 1)
             n = kMinWgPerCu;
@@ -560,21 +613,23 @@ int resident_wgs() {
     return cached[dev];
 }
 
-int gqa_rows_waves(const cp_gqa_args &a) {
-    const int G = a.Hq / a.Hkv;
-    int wg = kMinWgPerCu;
-    if (a.dt == CP_BF16) {
-        wg = G == 1 ? resident_wgs<2, 1>() : G == 2 ? resident_wgs<2, 2>()
-                   : G == 4 ? resident_wgs<2, 4>() : resident_wgs<2, 8>();
-    } else {
-        wg = G == 1 ? resident_wgs<4, 1>() : G == 2 ? resident_wgs<4, 2>()
-                   : G == 4 ? resident_wgs<4, 4>() : resident_wgs<4, 8>();
-    }
+template <bool kMtp>
+int rows_wgs(const cp_gqa_args &a, int G) {
+    if (a.dt == CP_BF16)
+        return G == 1 ? resident_wgs<2, 1, kMtp>() : G == 2 ? resident_wgs<2, 2, kMtp>()
+                      : G == 4 ? resident_wgs<2, 4, kMtp>() : resident_wgs<2, 8, kMtp>();
+    return G == 1 ? resident_wgs<4, 1, kMtp>() : G == 2 ? resident_wgs<4, 2, kMtp>()
+                  : G == 4 ? resident_wgs<4, 4, kMtp>() : resident_wgs<4, 8, kMtp>();
+}
+
+int gqa_rows_waves(const cp_gqa_args &a, int T, bool mtp) {
+    const int G = a.Hq / a.Hkv * T;
+    const int wg = mtp ? rows_wgs<true>(a, G) : rows_wgs<false>(a, G);
     return device_cus() * wg * kWaves;
 }
 
 cp_status gqa_rows_launch(const cp_gqa_args &a, int bs_log2, float *ws_o, float *ws_l,
-                          int32_t *seg, int32_t W, hipStream_t stream) {
+                          int32_t *seg, int32_t W, const GqaMtp &mtp, hipStream_t stream) {
     RowParams p;
     p.q = to_global(a.q);
     p.kc = to_global(a.k_cache);
@@ -592,7 +647,13 @@ cp_status gqa_rows_launch(const cp_gqa_args &a, int bs_log2, float *ws_o, float 
     p.ws_o = ws_o;
     p.ws_l = ws_l;
     p.seg = seg;
-    const int G = a.Hq / a.Hkv;
+    p.seq_len = mtp.seq_len;
+    p.T = mtp.T;
+    p.Greal = a.Hq / a.Hkv;
+    p.dcp_rank = mtp.dcp_rank;
+    p.dcp_size = mtp.dcp_size;
+    p.dcp_I = mtp.dcp_I;
+    const int G = a.Hq / a.Hkv * mtp.T;  // rows per KV head
     if (a.dt == CP_BF16) {
         switch (G) {
         case 1: return launch_rows<2, 1>(p, stream);

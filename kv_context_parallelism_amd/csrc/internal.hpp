@@ -39,6 +39,7 @@ struct GqaPlan {
     size_t ws_bytes;       // partial outputs + LSEs (+ segment table), 0 if none
 };
 GqaPlan plan_gqa(const cp_gqa_args &a);
+GqaPlan plan_gqa_mtp(const cp_gqa_mtp_args &m);
 
 struct MlaPlan {
     int32_t split_tokens;
@@ -71,17 +72,37 @@ struct MergeDesc {
     void *out;
     cp_dtype out_dt;
     float *lse_out;
+    // Output row of merge row r when remap_T > 1 (multi-token decode: merge
+    // rows are (request, KV head, token, head in group); outputs are
+    // [request][token][Hq]): see merge_out_row.
+    int32_t remap_T = 1, remap_G = 1, remap_Hkv = 1;
 };
 cp_status launch_merge(const MergeDesc &m, hipStream_t stream);
+
+__host__ __device__ inline int64_t merge_out_row(const MergeDesc &m, int64_t r) {
+    if (m.remap_T <= 1) return r;
+    const int64_t per = (int64_t)m.remap_T * m.remap_G;  // rows per (request, KV head)
+    const int64_t seg = r / per, sub = r - seg * per;
+    const int64_t b = seg / m.remap_Hkv, g = seg - b * m.remap_Hkv;
+    const int64_t t = sub / m.remap_G, h = sub - t * m.remap_G;
+    return (b * m.remap_T + t) * ((int64_t)m.remap_Hkv * m.remap_G) + g * m.remap_G + h;
+}
 
 // Compute units of the current device (cached per device).
 int device_cus();
 
 // Row-layout GQA decode kernel (256-byte KV rows), decode_gqa_rows.hip.
-bool gqa_rows_supported(const cp_gqa_args &a);
-int gqa_rows_waves(const cp_gqa_args &a);
+// T > 1: multi-token queries (the request's last T positions, causal on the
+// shard's interleaved positions); T = 1 with seq_len == nullptr: single token.
+struct GqaMtp {
+    int32_t T = 1;
+    const int32_t *seq_len = nullptr;
+    int32_t dcp_rank = 0, dcp_size = 1, dcp_I = 1;
+};
+bool gqa_rows_supported(const cp_gqa_args &a, int T = 1);
+int gqa_rows_waves(const cp_gqa_args &a, int T = 1, bool mtp = false);
 cp_status gqa_rows_launch(const cp_gqa_args &a, int bs_log2, float *ws_o, float *ws_l,
-                          int32_t *seg, int32_t W, hipStream_t stream);
+                          int32_t *seg, int32_t W, const GqaMtp &mtp, hipStream_t stream);
 
 // ---------------------------------------------------------------- device side
 

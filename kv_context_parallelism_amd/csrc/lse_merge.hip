@@ -139,13 +139,13 @@ __global__ void __launch_bounds__(kThreads) merge_lanes_kernel(MergeDesc m) {
                 u32x2 pk;
                 pk.x = pack_bf16x2(v.x, v.y);
                 pk.y = pack_bf16x2(v.z, v.w);
-                reinterpret_cast<u32x2 *>(m.out)[row * n4 + c] = pk;
+                reinterpret_cast<u32x2 *>(m.out)[merge_out_row(m, row) * n4 + c] = pk;
             } else {
-                reinterpret_cast<float4 *>(m.out)[row * n4 + c] = v;
+                reinterpret_cast<float4 *>(m.out)[merge_out_row(m, row) * n4 + c] = v;
             }
         }
         if (m.lse_out && lane_g == 0)
-            m.lse_out[row] = nan ? NAN : (empty ? -INFINITY : lmax + logf(asum));
+            m.lse_out[merge_out_row(m, row)] = nan ? NAN : (empty ? -INFINITY : lmax + logf(asum));
     }
 }
 
@@ -243,15 +243,15 @@ __global__ void __launch_bounds__(kThreads) merge_rows_kernel(MergeDesc m) {
                 u32x2 pk;
                 pk.x = pack_bf16x2(acc.x, acc.y);
                 pk.y = pack_bf16x2(acc.z, acc.w);
-                reinterpret_cast<u32x2 *>(m.out)[row * n4 + c] = pk;
+                reinterpret_cast<u32x2 *>(m.out)[merge_out_row(m, row) * n4 + c] = pk;
             } else {
-                reinterpret_cast<float4 *>(m.out)[row * n4 + c] = acc;
+                reinterpret_cast<float4 *>(m.out)[merge_out_row(m, row) * n4 + c] = acc;
             }
         }
         __syncthreads();
     }
     if (m.lse_out && tid == 0)
-        m.lse_out[row] = nan ? NAN : (lmax == -INFINITY ? -INFINITY : lmax + logf(asum));
+        m.lse_out[merge_out_row(m, row)] = nan ? NAN : (lmax == -INFINITY ? -INFINITY : lmax + logf(asum));
 }
 
 }  // namespace

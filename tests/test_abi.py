@@ -59,6 +59,7 @@ int main(void) {
   printf("cp_mla_args sizeof %zu\n", sizeof(cp_mla_args));
   printf("cp_prefill_args sizeof %zu\n", sizeof(cp_prefill_args));
   printf("cp_kv_gather_args sizeof %zu\n", sizeof(cp_kv_gather_args));
+  printf("cp_gqa_mtp_args sizeof %zu\n", sizeof(cp_gqa_mtp_args));
   %FIELDS%
   return 0;
 }
@@ -68,7 +69,8 @@ int main(void) {
 @pytest.mark.parametrize("cname,pytype", [("cp_gqa_args", _lib.CpGqaArgs),
                                           ("cp_mla_args", _lib.CpMlaArgs),
                                           ("cp_prefill_args", _lib.CpPrefillArgs),
-                                          ("cp_kv_gather_args", _lib.CpKvGatherArgs)])
+                                          ("cp_kv_gather_args", _lib.CpKvGatherArgs),
+                                          ("cp_gqa_mtp_args", _lib.CpGqaMtpArgs)])
 def test_struct_layout_matches_c(tmp_path, cname, pytype):
     fields = "\n".join(f"F({cname}, {f})" for f, _ in pytype._fields_)
     src = tmp_path / "layout.c"
@@ -210,3 +212,24 @@ def test_head_scatter_validation():
     assert b"part_stride" in lib.cp_last_error()
     assert lib.cp_lse_merge_packed(4, 10, 16, 16, 200, 16, 2, None, None) == 2
     assert lib.cp_lse_merge_packed(4, 10, 16, 24, 200, 16, 0, None, None) == 1
+
+
+def test_gqa_mtp_validation():
+    """The multi-token entry checks q_len, the DCP rank and interleave, the
+    sequence lengths and the supported row count on the host."""
+    lib = _lib.load()
+    base = _lib.CpGqaArgs(q=16, k_cache=16, v_cache=16, block_table=16, local_len=16, B=2, Hq=8,
+                          Hkv=2, D=128, bs=16, bt_stride=4, num_blocks=8, scale=0.1,
+                          dt=_lib.CP_BF16, out=16, lse=16)
+    good = dict(q_len=2, dcp_rank=1, dcp_size=4, interleave=16, seq_len=16)
+    for field, bad, code in [("q_len", 0, 1), ("dcp_rank", 4, 1), ("dcp_rank", -1, 1),
+                             ("dcp_size", 0, 1), ("interleave", 0, 1), ("seq_len", None, 1),
+                             ("q_len", 3, 2), ("q_len", 4, 2)]:
+        kw = dict(good)
+        kw[field] = bad
+        m = _lib.CpGqaMtpArgs(base=base, **kw)
+        assert lib.cp_decode_attn_partial_gqa_mtp(ctypes.byref(m), None, 0, None) == code, (field, bad)
+    # q_len 2 x group 4 = 8 rows per KV head: supported, so only the workspace is missing
+    m = _lib.CpGqaMtpArgs(base=base, **good)
+    assert lib.cp_decode_attn_partial_gqa_mtp(ctypes.byref(m), None, 0, None) == 3
+    assert lib.cp_workspace_bytes(_lib.CP_OP_DECODE_GQA_MTP, ctypes.byref(m)) > 0
