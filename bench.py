@@ -159,6 +159,7 @@ class GqaDecodeBench:
                                          + self.q.numel() * self.q.element_size()
                                          + w.B * T * w.Hq * (w.D + 1) * 4)
         self.work_step = self.kv_bytes_step
+        self.tokens_step = w.B * T  # query tokens decoded per step (one layer, all shards)
         self.per_launch_work = self.per_launch_bytes
         self.launches_per_step = w.N
         self.dominant = list(range(w.N))
@@ -299,6 +300,7 @@ class MlaDecodeBench:
         torch.cuda.synchronize()
         flop_tok = w.Hq * (w.D + w.Dv) * 2
         self.work_step = int(seq.sum()) * flop_tok
+        self.tokens_step = w.B  # decode tokens per step (one layer, all shards)
         self.per_launch_work = [int(sh["ll"].sum()) * flop_tok for sh in self.shards]
         eb = self.lat.element_size()
         self.per_launch_bytes = [int(sh["ll"].sum()) * w.D * eb + self.q.numel() * 2
@@ -410,6 +412,7 @@ class PrefillBench:
         self.work_causal = causal * w.Hq * 4 * w.D
         self.work_prefix = C * P * w.Hq * 4 * w.D
         self.work_step = self.work_causal + self.work_prefix
+        self.tokens_step = w.C  # prefill tokens per step (one layer, all PCP ranks)
         # events bracket every launch: per rank one causal-chunk call, then one
         # call per prefix shard; the prefix calls carry 80% of the work
         self.launches_per_step = w.N * (w.N + 1)
@@ -526,6 +529,7 @@ class DcpPrefillBench:
         causal = C * (C + 1) // 2
         # every (query, key) pair with key position <= query position, once
         self.work_step = (causal + C * P) * w.Hq * 4 * w.D
+        self.tokens_step = C  # prefill tokens per step (one layer, all ranks)
         # events bracket every shard call: per PCP rank one call per DCP shard
         self.launches_per_step = w.N * w.N
         self.dominant = list(range(w.N * w.N))
@@ -633,6 +637,7 @@ class KvGatherBench:
         row = w.Hkv * w.D * self.k.element_size()
         # K and V: every row read from its shard once and written once
         self.work_step = 2 * 2 * P * row
+        self.tokens_step = P  # tokens gathered per step
         self.per_launch_work = [self.work_step]
         self.per_launch_bytes = [self.work_step]
         self.launches_per_step = 1
@@ -725,6 +730,7 @@ class HeadScatterBench:
         self.work_pack = rows * (Dv + 1) * 4 + rows * (Dv + 4) * 4
         self.work_merge = (rows // N) * (N * (Dv + 1) * 4 + Dv * 2 + 4)
         self.work_step = self.layers * (self.work_correct + self.work_pack + self.work_merge)
+        self.tokens_step = None  # no token count: three exchange kernels of one rank
         self.per_launch_work = [self.work_pack]
         self.per_launch_bytes = [self.work_pack]
         self.launches_per_step = 3
@@ -878,6 +884,10 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": bench.dtype,
         "data": "synthetic", "config": bench.config(), "roofline": roof,
     }
+    if getattr(bench, "tokens_step", None):
+        # tokens of one layer of the whole (simulated) CP group per second: the
+        # N ranks' calls run one after another on this GPU
+        line["tokens_per_s"] = round(bench.tokens_step / (ms_step / 1e3), 1)
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on a bounded sample", file=sys.stderr, flush=True)
         v, sample = bench.cpu_baseline()

@@ -27,6 +27,10 @@
 // V product uses packed bf16 dot2 over token pairs (fp32 accumulate).
 // Loads are software-pipelined: the next tile's K is requested after this
 // tile's scores, its V after this tile's V product.
+//
+// Multi-token queries (a separate instantiation): the G rows per KV head are
+// q_len tokens x Hq/Hkv heads, and each row sees the shard's keys up to its
+// token's position; tiles past the first token's limit mask per row.
 #include <math.h>
 
 #include <type_traits>
