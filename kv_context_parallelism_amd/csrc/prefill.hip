@@ -66,6 +66,7 @@ constexpr float kLazy = 8.f;
 constexpr int kPf = 2;
 constexpr int kStages = kPf + 2;
 static_assert(kStages * 2 * kTileB <= 160 * 1024, "ring fits the LDS");
+static_assert((kStages & (kStages - 1)) == 0, "ring index by mask");
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -300,15 +301,18 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
         const int64_t rstride = kPaged ? (int64_t)kD * 2 : (int64_t)p.Hkv * kD * 2;
         return (uint32_t)(r16 * rstride) + (uint32_t)(((ln & 15) ^ swz(r16)) * 16);
     }();
-    auto group_row = [&](int32_t t) -> int64_t {  // base row of the 16-key group at key t
+    // Base row of the 16-key group at key t, in 32-bit arithmetic (the host
+    // checks that every row index of the source fits in 31 bits); one unsigned
+    // compare rejects negative and too large block ids.
+    auto group_row = [&](int32_t t) -> uint32_t {
         if constexpr (kPaged) {
-            int32_t phys = p.bt[t >> p.bs_log2];
-            const bool ok = phys >= 0 && (int64_t)phys < p.num_blocks;
+            uint32_t phys = (uint32_t)p.bt[t >> p.bs_log2];
+            const bool ok = phys < (uint32_t)p.num_blocks;
             bad |= !ok;
-            phys = ok ? phys : 0;
-            return ((int64_t)phys * p.Hkv + g) * bs + (t & (bs - 1) & ~15);
+            phys = ok ? phys : 0u;
+            return ((phys * (uint32_t)p.Hkv + (uint32_t)g) << p.bs_log2) + (uint32_t)(t & (bs - 1) & ~15);
         } else {
-            return (int64_t)(t & ~15) * p.Hkv + g;
+            return (uint32_t)(t & ~15) * (uint32_t)p.Hkv + (uint32_t)g;
         }
     };
     // Ping-pong.  Iteration it is one MFMA block -- the value product of tile
@@ -406,26 +410,35 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
     for (int32_t it = 0; it <= ntile; ++it) {  // it == ntile: the last value product only
         const bool pre = it + kPf < ntile;
         const int32_t jn = (it + kPf) * kBN;
-        const int bn = (it + kPf) % kStages;
+        const int bn = (it + kPf) & (kStages - 1);
         const bool spread = spread_ok && pre && jn + kBN <= kend;
-        int64_t ra = 0, rb2 = 0;
+        uint32_t ra = 0, rb2 = 0;
         if (spread) {  // scalar loads before the barrier that their latency then overlaps
             ra = group_row(jn + 16 * qa);
             rb2 = group_row(jn + 16 * qb2);
         }
         // tile it has landed (own copies; later tiles may still be in flight) ...
-        wait_copies_at_most(min(kPf - 1, ntile - 1 - it) * per_tile);
+        static_assert(kPf == 2, "the eight-wave wait below leaves one tile in flight");
+        if (nwaves == 8) {  // four copies per wave and tile
+            if (it + 1 < ntile) vm_wait<4>();
+            else vm_wait<0>();
+        } else {
+            wait_copies_at_most(min(kPf - 1, ntile - 1 - it) * per_tile);
+        }
         __syncthreads();  // ... for every wave; the buffer of tile it - 2 is free again
         // the block ids are needed from here on: wait for them now, while no
         // LDS read is in flight (the two share a wait counter)
         asm volatile("" ::"s"(ra), "s"(rb2));
         const uint32_t dstn = kv_lds + (uint32_t)(bn * 2 * kTileB) + (uint32_t)(wave * 1024);
+        // sources of this wave's four copies of tile it + kPf: K then V of its
+        // two 16-key groups
+        const gbyte *csrc[4] = {ksrc + ((uint64_t)ra << 8), ksrc + ((uint64_t)rb2 << 8),
+                                vsrc + ((uint64_t)ra << 8), vsrc + ((uint64_t)rb2 << 8)};
         // copy k of tile it + kPf goes after MFMA step 8 k + 7 of this block
         auto side = [&](int step) {
             if ((step & 7) != 7 || !spread) return;
             const int k = step >> 3;
-            const gbyte *src = ((k & 2) ? vsrc : ksrc) + ((k & 1) ? rb2 : ra) * (kD * 2);
-            dma16(src + off8, __builtin_amdgcn_readfirstlane(dstn + (uint32_t)(k * 8 * 1024)));
+            dma16(csrc[k] + off8, dstn + (uint32_t)(k * 8 * 1024));
         };
         if (pre && !spread) {
             const TileSrc ts = stage_rows(jn);
@@ -596,6 +609,8 @@ extern "C" cp_status pcp_prefill_attn_causal(const cp_prefill_args *a, void *ws,
         if (!a->k || !a->v) return fail(CP_E_INVALID, "prefill: dense source needs k and v");
         if (!aligned16(a->k) || !aligned16(a->v))
             return fail(CP_E_INVALID, "prefill: k/v must be 16-byte aligned");
+        if ((int64_t)a->C * a->Hkv >= ((int64_t)1 << 31))
+            return fail(CP_E_UNSUPPORTED, "prefill: %d x %d K/V rows exceed 2^31", a->C, a->Hkv);
         p.k = to_global(a->k);
         p.v = to_global(a->v);
     } else {  // CP_KV_PAGED or CP_KV_PAGED_CAUSAL
@@ -609,6 +624,9 @@ extern "C" cp_status pcp_prefill_attn_causal(const cp_prefill_args *a, void *ws,
                         a->bs);
         if (!aligned16(a->k_cache) || !aligned16(a->v_cache))
             return fail(CP_E_INVALID, "prefill: caches must be 16-byte aligned");
+        if (a->num_blocks < 0 || a->num_blocks * a->Hkv * a->bs >= ((int64_t)1 << 31))
+            return fail(CP_E_UNSUPPORTED, "prefill: %lld blocks x %d heads x %d rows exceed 2^31",
+                        (long long)a->num_blocks, a->Hkv, a->bs);
         p.kc = to_global(a->k_cache);
         p.vc = to_global(a->v_cache);
         p.bt = to_const(a->block_table);
