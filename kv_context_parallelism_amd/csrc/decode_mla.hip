@@ -16,12 +16,17 @@
 //     registers for the segment).  The value product is split by columns:
 //     wave w accumulates O[h][64 w .. 64 w + 63] for every head h, so each
 //     value column is read from LDS by one wave only.  The probabilities pass
-//     between the two through LDS (a second barrier per tile), together with
-//     each head's rescale factor.  The accumulators (128 x 64 fp32 outputs,
+//     between the two through LDS, together with each head's rescale factor.
+//     bf16: one barrier per tile -- after it, a wave runs the value product of
+//     the previous tile (its probabilities in one of two LDS buffers), then
+//     the scores of this tile (into the other buffer); fp8: a second barrier
+//     per tile between the scores and the value product of the same tile.  The accumulators (128 x 64 fp32 outputs,
 //     16 x 32 scores) and the queries fit a wave's 256 VGPRs; the file is
 //     compiled with MFMA results in VGPRs so that rescales update them in place;
-//   * 32-token latent tiles go HBM -> LDS by global_load_lds (no registers),
-//     triple-buffered: two tiles are in flight while the third is consumed.
+//   * 32-token latent tiles go HBM -> LDS by global_load_lds (no registers)
+//     into a ring of three: bf16 reads tiles it - 1 and it while tile it + 1
+//     is in flight (the second probability buffer leaves no room for a
+//     fourth); fp8 keeps two raw tiles in flight.
 //     The copies are issued from inline asm and waited for with explicit
 //     vmcnt counts, so the compiler does not serialise them against the LDS
 //     reads of the tile being consumed;
@@ -181,10 +186,12 @@ __global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
     __shared__ int32_t s_wsum[kWaves];
     // probabilities of the tile, [head][32 tokens in value-product k order]
     // (rows padded to 80 bytes: the 16-byte reads of 16 rows hit distinct banks)
-    __shared__ __attribute__((aligned(16))) uint8_t s_p[kHeadsWg * kPRow];
-    __shared__ __attribute__((aligned(16))) float s_alpha[kHeadsWg];  // rescale of each head's rows
+    // (bf16: two buffers, tile it's written while tile it - 1's are read)
+    constexpr int kPBufs = kFp8 ? 1 : 2;
+    __shared__ __attribute__((aligned(16))) uint8_t s_pp[kPBufs][kHeadsWg * kPRow];
+    __shared__ __attribute__((aligned(16))) float s_alphap[kPBufs][kHeadsWg];  // rescale of each head's rows
     __shared__ __attribute__((aligned(16))) float s_linv[kHeadsWg];   // 1 / row sum at the end
-    __shared__ __attribute__((aligned(8))) uint8_t s_flag[kWaves];    // a head of wave w rescaled
+    __shared__ __attribute__((aligned(8))) uint8_t s_flagp[kPBufs][kWaves];    // a head of wave w rescaled
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -398,7 +405,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
         // was rescaled to s_flag[wave].  The score product is pipelined by
         // hand, three LDS operands ahead, with a scheduling barrier per step.
         constexpr int kPre = 3;
-        auto scores_softmax = [&](int32_t it, const uint8_t *tile) {
+        auto scores_softmax = [&](int32_t it, const uint8_t *tile, int pb) {
+            uint8_t *s_p = s_pp[pb];
+            float *s_alpha = s_alphap[pb];
+            uint8_t *s_flag = s_flagp[pb];
             const int32_t tb = s0 + it * kT;
             // Per-lane addresses (16-lane group G = lane / 16, j = lane % 16),
             // recomputed per tile from a fresh lane id.  Score operand of half hf,
@@ -489,7 +499,10 @@ __global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
         // j / 4 and the same + 8, chunk 8 w + 4 cb + 2 g + (j % 4) / 2, byte
         // 8 (j % 2); the probabilities (A operand) are one 16-byte read per
         // (head block, k-step) from s_p, whose k order matches those rows.
-        auto value_product = [&](const uint8_t *tile) {
+        auto value_product = [&](const uint8_t *tile, int pb) {
+            const uint8_t *s_p = s_pp[pb];
+            const float *s_alpha = s_alphap[pb];
+            const uint8_t *s_flag = s_flagp[pb];
             // rescale the rows of every head whose owner raised its reference maximum
             const uint64_t flags = *reinterpret_cast<const uint64_t *>(s_flag);
             if (flags != 0) {
@@ -554,12 +567,12 @@ __global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
         };
         auto compute_tile = [&](int32_t it, const uint8_t *tile) {
             if (active) {
-                scores_softmax(it, tile);
+                scores_softmax(it, tile, 0);
             } else if (lane == 0) {
-                s_flag[wave] = 0;
+                s_flagp[0][wave] = 0;
             }
             __syncthreads();  // every head's probabilities and rescale factors are in LDS
-            value_product(tile);
+            value_product(tile, 0);
         };
 
         if constexpr (kFp8) {
@@ -580,13 +593,21 @@ __global__ void __launch_bounds__(kThreads, 1) mla_kernel(MlaParams p) {
                 compute_tile(it, s_kv[it % 2]);
             }
         } else {
+            // one barrier per tile: iteration it runs the value product of
+            // tile it - 1 (probabilities of buffer (it - 1) % 2) and then the
+            // scores of tile it (into buffer it % 2); ring of 3, tile it + 1 in
+            // flight
             if (ntile > 0) issue_tile(0);
-            if (ntile > 1) issue_tile(1);
-            for (int32_t it = 0; it < ntile; ++it) {
-                wait_all_but_one_tile<kBfSlots>(it + 1 < ntile, wave);
-                __syncthreads();  // tile it landed for all waves; buffer of it - 1 free
-                if (it + 2 < ntile) issue_tile(it + 2);
-                compute_tile(it, s_kv[it % 3]);
+            for (int32_t it = 0; it <= ntile; ++it) {
+                vm_wait<0>();     // tile it has landed (own copies) ...
+                __syncthreads();  // ... for every wave; tile it - 1's probabilities are in
+                                  // LDS, and tile it - 2's buffer is free
+                if (it + 1 < ntile) issue_tile(it + 1);
+                if (it >= 1) value_product(s_kv[(it - 1) % 3], (it - 1) & 1);
+                if (it < ntile) {
+                    if (active) scores_softmax(it, s_kv[it % 3], it & 1);
+                    else if (lane == 0) s_flagp[it & 1][wave] = 0;
+                }
             }
         }
 
