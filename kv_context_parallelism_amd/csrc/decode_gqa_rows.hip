@@ -7,8 +7,8 @@
 // shard-normalised output o_i and L_i = log sum_j exp(s_j).
 //
 // Work distribution.  The (request, KV head, 32-token chunk) space is laid
-// out flat, request-major.  Exactly W waves are launched (W = what the chip
-// holds at once) and wave w takes the contiguous chunk range
+// out flat, request-major.  Exactly W waves are launched (four per CU, all
+// resident at once) and wave w takes the contiguous chunk range
 // [w*R/W, (w+1)*R/W) of the R chunks, so every wave streams the same number of
 // KV bytes whatever the mix of context lengths.  A wave whose range crosses
 // from one (request, KV head) into the next writes one partial per piece to
@@ -45,10 +45,13 @@ constexpr int kWaves = 4;       // waves per workgroup
 constexpr int kTile = 32;       // tokens per tile = per scheduling chunk
 constexpr int kNG = kTile / 16; // 16-token groups per tile
 constexpr int kMaxB = 8192;     // requests handled by the in-LDS prefix sum
-// Register bound for the compiler: at least 2 workgroups per CU.  The number
-// actually resident (3 when the kernel needs <= 168 VGPRs) is queried at run
-// time and sets how many waves the schedule spreads the work over.
+// Register bound for the compiler: at least 2 workgroups per CU.
 constexpr int kMinWgPerCu = 2;
+// Workgroups the schedule spreads the work over, per CU.  One (a wave per
+// SIMD) measured faster than filling the CU with the 2-3 that fit: each
+// (request, KV head) is split into fewer partials for the combine, and the
+// four waves' loads in flight already keep HBM busy.
+constexpr int kSchedWgPerCu = 1;
 
 struct RowParams {
     const gbyte *q, *kc, *vc;
@@ -600,36 +603,11 @@ bool gqa_rows_supported(const cp_gqa_args &a, int T) {
     return row256 && (G == 1 || G == 2 || G == 4 || G == 8) && a.B <= kMaxB;
 }
 
-template <int EB, int G, bool kMtp>
-int resident_wgs() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &n, reinterpret_cast<const void *>(gqa_rows_kernel<EB, G, kMinWgPerCu, kMtp>),
-                64 * kWaves, 0) != hipSuccess ||
-            n < 1)
-            n = kMinWgPerCu;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
-
-template <bool kMtp>
-int rows_wgs(const cp_gqa_args &a, int G) {
-    if (a.dt == CP_BF16)
-        return G == 1 ? resident_wgs<2, 1, kMtp>() : G == 2 ? resident_wgs<2, 2, kMtp>()
-                      : G == 4 ? resident_wgs<2, 4, kMtp>() : resident_wgs<2, 8, kMtp>();
-    return G == 1 ? resident_wgs<4, 1, kMtp>() : G == 2 ? resident_wgs<4, 2, kMtp>()
-                  : G == 4 ? resident_wgs<4, 4, kMtp>() : resident_wgs<4, 8, kMtp>();
-}
-
 int gqa_rows_waves(const cp_gqa_args &a, int T, bool mtp) {
-    const int G = a.Hq / a.Hkv * T;
-    const int wg = mtp ? rows_wgs<true>(a, G) : rows_wgs<false>(a, G);
-    return device_cus() * wg * kWaves;
+    (void)a;
+    (void)T;
+    (void)mtp;
+    return device_cus() * kSchedWgPerCu * kWaves;
 }
 
 cp_status gqa_rows_launch(const cp_gqa_args &a, int bs_log2, float *ws_o, float *ws_l,
