@@ -275,10 +275,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
 
-#ifndef PF_PRE
-#define PF_PRE 3
-#endif
-    constexpr int kPre = PF_PRE;
+    constexpr int kPre = 3;  // LDS operands requested ahead of their MFMA
     const int ntile = kend > 0 ? (kend + kBN - 1) / kBN : 0;
     const int ntile_w = kend_w > 0 ? (kend_w + kBN - 1) / kBN : 0;  // a prefix of the tiles
     const int per_tile = kSlots / nwaves;  // this wave's copies per tile (nwaves divides 32)
