@@ -281,16 +281,19 @@ void launch_lanes(const MergeDesc &m, hipStream_t stream) {
 }
 
 // float4 columns -> (lanes per row, columns per lane).  Returns false (the
-// caller then uses the block kernel) when the rows are too wide, or too few
-// to keep enough column loads in flight on every CU (lanes times columns per
-// lane: a row of 128 float4 columns in 64 lanes counts twice).
+// caller then uses the block kernel) when the rows are too wide, or -- for a
+// plain merge -- too few to keep enough column loads in flight on every CU
+// (lanes times columns per lane: a row of 128 float4 columns in 64 lanes
+// counts twice).  A split combine (segment table) always takes it: its rows
+// have a few parts each, which one batch of loads covers, and that beats the
+// block kernel's dependent passes even on 1,024 rows (GQA decode combine).
 template <bool kBf16Out>
 bool launch_lanes_for(const MergeDesc &m, hipStream_t stream) {
     const int n4 = m.Dv / 4;
     int S = 1;
     while (S < n4 && S < 64) S *= 2;
     const int cols = (n4 + S - 1) / S;
-    if (m.rows * S * cols < (int64_t)device_cus() * 512) return false;
+    if (!m.seg && m.rows * S * cols < (int64_t)device_cus() * 512) return false;
     if (n4 <= 1) launch_lanes<kBf16Out, 1, 1>(m, stream);
     else if (n4 <= 2) launch_lanes<kBf16Out, 2, 1>(m, stream);
     else if (n4 <= 4) launch_lanes<kBf16Out, 4, 1>(m, stream);
