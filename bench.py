@@ -161,8 +161,10 @@ class GqaDecodeBench:
         self.work_step = self.kv_bytes_step
         self.tokens_step = w.B * T  # query tokens decoded per step (one layer, all shards)
         self.per_launch_work = self.per_launch_bytes
-        self.launches_per_step = w.N
+        self.launches_per_step = w.N + 1  # the N shard partials, then the merge
         self.dominant = list(range(w.N))
+        self.merge_idx = w.N
+        self.merge_bytes = (w.N + 1) * w.B * T * w.Hq * (w.D + 1) * 4
         self.kernel_name = ("cp_decode_attn_partial_gqa (attention + split combine)" if T == 1 else
                             f"cp_decode_attn_partial_gqa_mtp ({T} query tokens; attention + split "
                             "combine)")
@@ -188,7 +190,11 @@ class GqaDecodeBench:
                                                   workspace=sh["ws"])
             if ev is not None:
                 ev[r][1].record()
+        if ev is not None:
+            ev[w.N][0].record()
         cp.cp_lse_merge(self.part_out, self.part_lse, out=self.out, lse_out=self.lse)
+        if ev is not None:
+            ev[w.N][1].record()
 
     def cpu_baseline(self, budget_s=15.0):
         """The fp64 oracle on the same workload: all shard partials of whole
@@ -305,8 +311,10 @@ class MlaDecodeBench:
         eb = self.lat.element_size()
         self.per_launch_bytes = [int(sh["ll"].sum()) * w.D * eb + self.q.numel() * 2
                                  + w.B * w.Hq * (w.Dv + 1) * 4 for sh in self.shards]
-        self.launches_per_step = w.N
+        self.launches_per_step = w.N + 1  # the N shard partials, then the merge
         self.dominant = list(range(w.N))
+        self.merge_idx = w.N
+        self.merge_bytes = (w.N + 1) * w.B * w.Hq * (w.Dv + 1) * 4
         self.kernel_name = "cp_decode_attn_partial_mla (attention + split combine)"
         self.dtype = "bf16"
 
@@ -324,7 +332,11 @@ class MlaDecodeBench:
                                           lse=self.part_lse[r], workspace=sh["ws"])
             if ev is not None:
                 ev[r][1].record()
+        if ev is not None:
+            ev[w.N][0].record()
         cp.cp_lse_merge(self.part_out, self.part_lse, out=self.out, lse_out=self.lse)
+        if ev is not None:
+            ev[w.N][1].record()
 
     def cpu_baseline(self, budget_s=15.0):
         """The fp64 oracle on the same workload: shard partials of request 0,
@@ -878,12 +890,20 @@ def main():
             roof["secondary"].append({"kernel": name, "avg_launch_us": round(sec_s * 1e6, 2),
                                       "achieved": round(work / sec_s / scale_v, 2),
                                       "frac": round(work / sec_s / scale_v / peak, 4)})
+    merge = None
+    if getattr(bench, "merge_idx", None) is not None:
+        m_ms = [step[bench.merge_idx][0].elapsed_time(step[bench.merge_idx][1]) for step in ev]
+        m_s = sum(m_ms) / len(m_ms) / 1e3
+        merge = {"kernel": "cp_lse_merge of the N shard partials", "avg_launch_us": round(m_s * 1e6, 2),
+                 "gbs": round(bench.merge_bytes / m_s / 1e9, 2)}
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": bench.dtype,
         "data": "synthetic", "config": bench.config(), "roofline": roof,
     }
+    if merge is not None:
+        line["merge"] = merge
     if getattr(bench, "tokens_step", None):
         # tokens of one layer of the whole (simulated) CP group per second: the
         # N ranks' calls run one after another on this GPU
