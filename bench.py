@@ -5,7 +5,8 @@ Default workload (--workload gqa_decode_bf16): one DCP decode step of a GQA
 model, bf16, 32 requests with contexts uniform in [4K, 32K], 32 query / 8 KV
 heads, head dim 128, KV sharded over 8 simulated DCP ranks (interleave 16,
 block size 16).  One step =
-  for every rank r: cp_slot_map + cp_cache_write of the step's new tokens,
+  for every rank r: the slot map and cache write of the step's new tokens
+                   (cp_slot_map_cache_write: both in one launch),
   for every rank r: cp_decode_attn_partial_gqa over shard r,
   then cp_lse_merge of the 8 partials.
 value = KV bytes the step reads / step time (GB/s).
@@ -173,9 +174,9 @@ class GqaDecodeBench:
     def step(self, ev=None):
         cp, w = self.cp, self.w
         for r, sh in enumerate(self.shards):
-            cp.cp_slot_map(self.req_new, self.pos_new, sh["bt_d"], r, w.N, w.I, w.bs,
-                           out=sh["slots"])
-            cp.cp_cache_write(sh["slots"], self.k_new, self.v_new, sh["kc"], sh["vc"], w.bs)
+            cp.cp_slot_map_cache_write(self.req_new, self.pos_new, sh["bt_d"], r, w.N, w.I, w.bs,
+                                       self.k_new, self.v_new, sh["kc"], sh["vc"],
+                                       slot_out=sh["slots"])
         for r, sh in enumerate(self.shards):
             if ev is not None:
                 ev[r][0].record()
@@ -321,9 +322,8 @@ class MlaDecodeBench:
     def step(self, ev=None):
         cp, w = self.cp, self.w
         for r, sh in enumerate(self.shards):
-            cp.cp_slot_map(self.req_new, self.pos_new, sh["bt_d"], r, w.N, w.I, w.bs,
-                           out=sh["slots"])
-            cp.cp_cache_write(sh["slots"], self.lat_new, None, sh["kc"], None, w.bs)
+            cp.cp_slot_map_cache_write(self.req_new, self.pos_new, sh["bt_d"], r, w.N, w.I, w.bs,
+                                       self.lat_new, None, sh["kc"], None, slot_out=sh["slots"])
         for r, sh in enumerate(self.shards):
             if ev is not None:
                 ev[r][0].record()
@@ -442,8 +442,8 @@ class PrefillBench:
         cp, w = self.cp, self.w
         # the chunk's new K/V into the DCP shards (positions P .. P+C-1)
         for s, sh in enumerate(self.shards):
-            cp.cp_slot_map(self.req_c, self.pos_c, sh["bt_d"], s, w.N, w.I, w.bs, out=sh["slots"])
-            cp.cp_cache_write(sh["slots"], self.k, self.v, sh["kc"], sh["vc"], w.bs)
+            cp.cp_slot_map_cache_write(self.req_c, self.pos_c, sh["bt_d"], s, w.N, w.I, w.bs,
+                                       self.k, self.v, sh["kc"], sh["vc"], slot_out=sh["slots"])
         k = 0
         for r in range(w.N):
             if ev is not None:
@@ -557,8 +557,8 @@ class DcpPrefillBench:
         cp, w = self.cp, self.w
         # the chunk's K/V into the DCP shards (positions P .. P+C-1), interleaved
         for s, sh in enumerate(self.shards):
-            cp.cp_slot_map(self.req_c, self.pos_c, sh["bt_d"], s, w.N, w.I, w.bs, out=sh["slots"])
-            cp.cp_cache_write(sh["slots"], self.k_c, self.v_c, sh["kc"], sh["vc"], w.bs)
+            cp.cp_slot_map_cache_write(self.req_c, self.pos_c, sh["bt_d"], s, w.N, w.I, w.bs,
+                                       self.k_c, self.v_c, sh["kc"], sh["vc"], slot_out=sh["slots"])
         k = 0
         for r in range(w.N):
             for s, sh in enumerate(self.shards):

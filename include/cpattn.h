@@ -110,6 +110,19 @@ cp_status cp_cache_write(int64_t T, const int64_t *slot, const void *k, const vo
                          int32_t n_kv_heads, int32_t row_dim, cp_dtype dt, void *k_cache,
                          void *v_cache, int64_t num_blocks, int32_t bs, hipStream_t stream);
 
+/* cp_slot_map followed by cp_cache_write in one launch (the same two steps of
+ * [P1] section 2 and [P3] Deep Dive 4-5 for a step's new tokens): every token's
+ * slot is computed as cp_slot_map computes it and its rows are copied as
+ * cp_cache_write copies them; the results are identical to the two calls.
+ * Arguments are those of the two calls; slot_out [T] int64 may be NULL (the
+ * slots are then not stored).  Errors: those of both calls. */
+cp_status cp_slot_map_cache_write(int32_t T, const int32_t *req, const int32_t *pos,
+                                  const int32_t *block_table, int32_t B, int32_t bt_stride,
+                                  int32_t max_blocks, int32_t rank, int32_t N, int32_t I,
+                                  int32_t bs, int64_t *slot_out, const void *k, const void *v,
+                                  int32_t n_kv_heads, int32_t row_dim, cp_dtype dt, void *k_cache,
+                                  void *v_cache, int64_t num_blocks, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Rank-local decode attention: partial output + LSE
  * ([P3] Deep Dive 6, "Deriving the partial and global outputs": every rank

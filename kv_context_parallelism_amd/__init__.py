@@ -125,6 +125,30 @@ def cp_cache_write(slot, k, v, k_cache, v_cache, bs: int, stream=None):
                               _ptr(v_cache), num_blocks, bs, _stream(stream)), "cp_cache_write")
 
 
+def cp_slot_map_cache_write(req, pos, block_table, rank: int, N: int, I: int, bs: int, k, v,
+                            k_cache, v_cache, max_blocks=None, slot_out=None, stream=None):
+    """cp_slot_map then cp_cache_write in one launch (same results); the slots
+    go to ``slot_out`` (int64 [T]) when it is given."""
+    lib = _lib.load()
+    T = req.numel()
+    B, stride = block_table.shape
+    mb = stride if max_blocks is None else max_blocks
+    if v is None:
+        heads, row = 1, k.shape[-1]
+    else:
+        heads, row = k.shape[1], k.shape[2]
+    if k.dtype != k_cache.dtype or (v is not None and v.dtype != v_cache.dtype):
+        raise ValueError("rows and cache must share a dtype")
+    if slot_out is not None and slot_out.dtype != torch.int64:
+        raise ValueError("slot_out must be int64")
+    _check(lib.cp_slot_map_cache_write(T, _i32(req, "req"), _i32(pos, "pos"),
+                                       _i32(block_table, "block_table"), B, stride, mb, rank, N, I,
+                                       bs, _ptr(slot_out), _ptr(k), _ptr(v), heads, row, _dt(k),
+                                       _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
+                                       _stream(stream)), "cp_slot_map_cache_write")
+    return slot_out
+
+
 # ---------------------------------------------------------------------------
 # decode partials
 # ---------------------------------------------------------------------------

@@ -62,6 +62,9 @@ SIGNATURES = {
     "cp_slot_map": (_int, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp,
                            _vp]),
     "cp_cache_write": (_int, [_i64, _vp, _vp, _vp, _i32, _i32, _int, _vp, _vp, _i64, _i32, _vp]),
+    "cp_slot_map_cache_write": (_int, [_i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                       _i32, _vp, _vp, _vp, _i32, _i32, _int, _vp, _vp, _i64,
+                                       _vp]),
     "cp_decode_attn_partial_gqa": (_int, [ctypes.POINTER(CpGqaArgs), _vp, ctypes.c_size_t, _vp]),
     "cp_decode_attn_partial_gqa_mtp": (_int, [ctypes.POINTER(CpGqaMtpArgs), _vp, ctypes.c_size_t,
                                               _vp]),

@@ -31,6 +31,20 @@ __global__ void local_lens_kernel(int32_t B, const int32_t *__restrict__ seq_len
     if (b < B) out[b] = local_len_of(seq_lens[b], rank, N, I);
 }
 
+// Slot of token (request b, position t) on `rank`, or a sentinel: not this
+// rank's position (-1), or an invalid request, position or local block (-2).
+__device__ __forceinline__ int64_t slot_of(int32_t b, int32_t t, const int32_t *__restrict__ block_table,
+                                           int32_t B, int32_t bt_stride, int32_t max_blocks,
+                                           int32_t rank, int32_t N, int32_t I, int32_t bs) {
+    if (b < 0 || b >= B || t < 0) return CP_SLOT_INVALID;
+    const int32_t group = t / I;         // interleave group of the position
+    if (group % N != rank) return CP_SLOT_NOT_MINE;  // owner = floor(t / I) mod N
+    const int32_t l = (group / N) * I + (t - group * I);  // l <= t, fits in 32 bits
+    const int32_t blk = l / bs;
+    if (blk >= max_blocks) return CP_SLOT_INVALID;
+    return (int64_t)block_table[(int64_t)b * bt_stride + blk] * bs + (l - blk * bs);
+}
+
 __global__ void slot_map_kernel(int32_t T, const int32_t *__restrict__ req,
                                 const int32_t *__restrict__ pos,
                                 const int32_t *__restrict__ block_table, int32_t B,
@@ -38,31 +52,9 @@ __global__ void slot_map_kernel(int32_t T, const int32_t *__restrict__ req,
                                 int32_t I, int32_t bs, int64_t *__restrict__ slot_out) {
     int32_t j = blockIdx.x * blockDim.x + threadIdx.x;
     if (j >= T) return;
-    int32_t b = req[j];
-    int32_t t = pos[j];
-    if (b < 0 || b >= B || t < 0) {
-        slot_out[j] = CP_SLOT_INVALID;
-        return;
-    }
-    int32_t group = t / I;           // interleave group of the position
-    if (group % N != rank) {         // owner = floor(t / I) mod N
-        slot_out[j] = CP_SLOT_NOT_MINE;
-        return;
-    }
-    // local index: I tokens per complete round before this one, plus the offset
-    // inside the group
-    const int32_t l = (group / N) * I + (t - group * I);  // l <= t, fits in 32 bits
-    const int32_t blk = l / bs;
-    if (blk >= max_blocks) {
-        slot_out[j] = CP_SLOT_INVALID;
-        return;
-    }
-    slot_out[j] = (int64_t)block_table[(int64_t)b * bt_stride + blk] * bs + (l - blk * bs);
+    slot_out[j] = slot_of(req[j], pos[j], block_table, B, bt_stride, max_blocks, rank, N, I, bs);
 }
 
-// One thread per 16-byte chunk of a token's rows (all heads).  Index math is
-// 32-bit (the host splits launches so that a launch covers < 2^31 chunks);
-// slots are split into (block, offset) by a shift when bs is a power of two.
 __global__ void cache_write_kernel(int32_t T, const int64_t *__restrict__ slot,
                                    const u32x4 *__restrict__ k, const u32x4 *__restrict__ v,
                                    uint32_t n_heads, uint32_t row_chunks,
@@ -91,6 +83,43 @@ __global__ void cache_write_kernel(int32_t T, const int64_t *__restrict__ slot,
     if (v) v_cache[dst] = v[src];
 }
 
+
+// Both steps in one launch: thread (token j, 16-byte chunk c) computes the
+// token's slot itself (a few integer operations), the chunk-0 thread stores it
+// when slot_out is given, and every thread copies its chunk like
+// cache_write_kernel.
+__global__ void slot_map_write_kernel(int32_t T, const int32_t *__restrict__ req,
+                                      const int32_t *__restrict__ pos,
+                                      const int32_t *__restrict__ block_table, int32_t B,
+                                      int32_t bt_stride, int32_t max_blocks, int32_t rank,
+                                      int32_t N, int32_t I, int32_t bs, int64_t *__restrict__ slot_out,
+                                      const u32x4 *__restrict__ k, const u32x4 *__restrict__ v,
+                                      uint32_t n_heads, uint32_t row_chunks,
+                                      u32x4 *__restrict__ k_cache, u32x4 *__restrict__ v_cache,
+                                      int64_t num_slots, int32_t bs_log2) {
+    const uint32_t per_tok = n_heads * row_chunks;
+    const uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
+    const uint32_t j = idx / per_tok;
+    if (j >= (uint32_t)T) return;
+    const uint32_t c = idx - j * per_tok;
+    const int64_t s = slot_of(req[j], pos[j], block_table, B, bt_stride, max_blocks, rank, N, I, bs);
+    if (c == 0 && slot_out) slot_out[j] = s;
+    if (s < 0 || s >= num_slots) return;
+    const uint32_t h = c / row_chunks;
+    const uint32_t cc = c - h * row_chunks;
+    int64_t blk, off;
+    if (bs_log2 >= 0) {
+        blk = s >> bs_log2;
+        off = s & (bs - 1);
+    } else {
+        blk = s / bs;
+        off = s - blk * bs;
+    }
+    const int64_t dst = ((blk * n_heads + h) * bs + off) * row_chunks + cc;
+    const int64_t src = (int64_t)j * per_tok + c;
+    k_cache[dst] = k[src];
+    if (v) v_cache[dst] = v[src];
+}
 }  // namespace cpattn
 
 using namespace cpattn;
@@ -163,4 +192,53 @@ extern "C" cp_status cp_cache_write(int64_t T, const int64_t *slot, const void *
                            num_blocks * bs, bs, bs_log2);
     }
     return check_launch("cp_cache_write");
+}
+
+extern "C" cp_status cp_slot_map_cache_write(int32_t T, const int32_t *req, const int32_t *pos,
+                                             const int32_t *block_table, int32_t B,
+                                             int32_t bt_stride, int32_t max_blocks, int32_t rank,
+                                             int32_t N, int32_t I, int32_t bs, int64_t *slot_out,
+                                             const void *k, const void *v, int32_t n_kv_heads,
+                                             int32_t row_dim, cp_dtype dt, void *k_cache,
+                                             void *v_cache, int64_t num_blocks, hipStream_t stream) {
+    clear_error();
+    const int eb = elem_bytes(dt);
+    if (T < 0 || B < 1 || N < 1 || I < 1 || bs < 1 || rank < 0 || rank >= N || max_blocks < 1 ||
+        max_blocks > bt_stride || n_kv_heads < 1 || row_dim < 1 || num_blocks < 0 || eb == 0)
+        return fail(CP_E_INVALID,
+                    "cp_slot_map_cache_write: T=%d B=%d N=%d I=%d bs=%d rank=%d max_blocks=%d "
+                    "bt_stride=%d heads=%d row_dim=%d num_blocks=%lld",
+                    T, B, N, I, bs, rank, max_blocks, bt_stride, n_kv_heads, row_dim,
+                    (long long)num_blocks);
+    if ((v == nullptr) != (v_cache == nullptr))
+        return fail(CP_E_INVALID, "cp_slot_map_cache_write: give both v and v_cache, or neither");
+    if (((int64_t)row_dim * eb) % 16 != 0)
+        return fail(CP_E_UNSUPPORTED,
+                    "cp_slot_map_cache_write: row of %d bytes is not a multiple of 16", row_dim * eb);
+    if (T == 0) return CP_OK;
+    if (!req || !pos || !block_table || !k || !k_cache)
+        return fail(CP_E_INVALID, "cp_slot_map_cache_write: NULL pointer");
+    if (!aligned16(k) || !aligned16(k_cache) || (v && (!aligned16(v) || !aligned16(v_cache))))
+        return fail(CP_E_INVALID, "cp_slot_map_cache_write: data pointers must be 16-byte aligned");
+    const int32_t row_chunks = (int32_t)(((int64_t)row_dim * eb) / 16);
+    const int64_t per_tok = (int64_t)n_kv_heads * row_chunks;
+    if (per_tok > (1 << 20)) return fail(CP_E_UNSUPPORTED, "cp_slot_map_cache_write: rows too wide");
+    int bs_log2 = -1;
+    if ((bs & (bs - 1)) == 0)
+        for (bs_log2 = 0; (1 << bs_log2) < bs; ++bs_log2) {
+        }
+    // launches of < 2^31 chunks each
+    const int64_t tok_per_launch = ((int64_t)1 << 30) / per_tok;
+    for (int64_t t0 = 0; t0 < T; t0 += tok_per_launch) {
+        const int32_t tn = (int32_t)(T - t0 < tok_per_launch ? T - t0 : tok_per_launch);
+        const int64_t total = (int64_t)tn * per_tok;
+        const u32x4 *kp = (const u32x4 *)k + t0 * per_tok;
+        const u32x4 *vp = v ? (const u32x4 *)v + t0 * per_tok : nullptr;
+        hipLaunchKernelGGL(slot_map_write_kernel, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0,
+                           stream, tn, req + t0, pos + t0, block_table, B, bt_stride, max_blocks,
+                           rank, N, I, bs, slot_out ? slot_out + t0 : nullptr, kp, vp,
+                           (uint32_t)n_kv_heads, (uint32_t)row_chunks, (u32x4 *)k_cache,
+                           (u32x4 *)v_cache, num_blocks * bs, bs_log2);
+    }
+    return check_launch("cp_slot_map_cache_write");
 }

@@ -126,6 +126,32 @@ def test_host_validation_rejects_bad_arguments():
         assert b"scale" in lib.cp_last_error()
 
 
+def test_fused_slot_map_cache_write_validation():
+    """The fused call rejects what either of its two steps rejects."""
+    lib = _lib.load()
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    args = [4, fake, fake, fake, 1, 4, 4, 0, 4, 4, 16, None, fake, fake, 2, 64, 1, fake, fake, 8,
+            None]
+    bad = list(args)
+    bad[7] = 4  # rank outside [0, N)
+    assert lib.cp_slot_map_cache_write(*bad) == 1
+    bad = list(args)
+    bad[6] = 5  # max_blocks past the block-table width
+    assert lib.cp_slot_map_cache_write(*bad) == 1
+    bad = list(args)
+    bad[18] = None  # v without v_cache
+    assert lib.cp_slot_map_cache_write(*bad) == 1
+    bad = list(args)
+    bad[15] = 4  # a 4-element bf16 row is 8 bytes, not a multiple of 16
+    assert lib.cp_slot_map_cache_write(*bad) == 2
+    bad = list(args)
+    bad[1] = None  # req missing
+    assert lib.cp_slot_map_cache_write(*bad) == 1
+    bad = list(args)
+    bad[0] = 0  # nothing to do
+    assert lib.cp_slot_map_cache_write(*bad) == 0
+
+
 def test_mla_validation_rejects_unsupported_head_counts():
     """The MLA kernel covers up to 128 heads (four waves of 32) in multiples of
     16; other head counts are refused on the host, before any device call."""
