@@ -326,8 +326,10 @@ typedef struct cp_prefill_args {
  *    ([P1] section 2).  local_len bounds the keys (at least cnt(P + C));
  *    merging the dcp_size shards' partials gives the causal attention over
  *    prefix and chunk.
- * Supported: D = 128, Hq/Hkv in {1, 2, 4, 8}, bf16; K/V sources of fewer than
- * 2^31 rows of D (C x Hkv dense, num_blocks x Hkv x bs paged).
+ * Supported: any C that is a multiple of 2*pcp_size (pieces of any length: the
+ * pages' PCP2 example with C = 8 gives pieces of 2 rows); D = 128, Hq/Hkv in
+ * {1, 2, 4, 8}, bf16; K/V sources of fewer than 2^31 rows of D (C x Hkv
+ * dense, num_blocks x Hkv x bs paged); paged block sizes a power of two >= 16.
  * Workspace: none needed (cp_workspace_bytes returns 0).
  * Errors: CP_E_INVALID (C % (2*pcp_size), rank, sizes, pointers, a scale
  * that is not positive and finite; for CP_KV_PAGED_CAUSAL a dcp_rank outside

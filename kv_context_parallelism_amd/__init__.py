@@ -76,6 +76,67 @@ def _i32(t, name):
     return _ptr(t)
 
 
+# Shape and dtype checks of the binding.  The kernels trust the sizes they are
+# given (a cache's block dimension, a buffer's row count), so a tensor whose
+# shape disagrees with them would be read or written out of bounds: every
+# wrapper checks its tensors here, before any pointer is taken.
+
+def _shape(t, shape, name, dtype=None):
+    """t must have exactly ``shape`` (None entries match any size) and, if given,
+    ``dtype``."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dim() != len(shape) or any(s is not None and t.shape[i] != s
+                                    for i, s in enumerate(shape)):
+        want = "[" + ", ".join("*" if s is None else str(s) for s in shape) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}, expected {want}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _count(t, n, name, dtype=torch.int32):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.numel() != n:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _block_table(bt, B, name="block_table"):
+    """A 2-D int32 table with a row for each of the B requests."""
+    if bt is None or bt.dim() != 2 or bt.dtype != torch.int32:
+        raise ValueError(f"{name} must be a 2-D int32 tensor")
+    if bt.shape[0] < B or bt.shape[1] < 1:
+        raise ValueError(f"{name} has shape {list(bt.shape)}: needs {B} rows of at least one "
+                         "block")
+
+
+def _rows_and_caches(T, k, v, k_cache, v_cache, bs):
+    """Token rows and paged caches of a cache write: GQA k, v [T][Hkv][D] into
+    caches [num_blocks][Hkv][bs][D]; MLA k [T][Dk] (or [T][1][Dk]) into a
+    latent cache [num_blocks][bs][Dk].  Returns (heads, row elements)."""
+    if (v is None) != (v_cache is None):
+        raise ValueError("v and v_cache must both be given (GQA) or both be None (MLA)")
+    if v is None:
+        if k_cache.dim() != 3:
+            raise ValueError(f"latent cache has shape {list(k_cache.shape)}, expected "
+                             "[num_blocks, bs, Dk]")
+        row = k_cache.shape[2]
+        if k.dim() == 3:
+            _shape(k, (T, 1, row), "k")
+        else:
+            _shape(k, (T, row), "k")
+        _shape(k_cache, (None, bs, row), "k_cache", k.dtype)
+        return 1, row
+    _shape(k, (T, None, None), "k")
+    heads, row = k.shape[1], k.shape[2]
+    _shape(v, tuple(k.shape), "v", k.dtype)
+    _shape(k_cache, (None, heads, bs, row), "k_cache", k.dtype)
+    _shape(v_cache, tuple(k_cache.shape), "v_cache", k.dtype)
+    return heads, row
+
+
 # ---------------------------------------------------------------------------
 # ownership and paging
 # ---------------------------------------------------------------------------
@@ -86,6 +147,7 @@ def cp_local_seq_lens(seq_lens, rank: int, N: int, I: int, out=None, stream=None
     B = seq_lens.numel()
     if out is None:
         out = torch.empty(B, dtype=torch.int32, device=seq_lens.device)
+    _count(out, B, "out")
     _check(lib.cp_local_seq_lens(B, _i32(seq_lens, "seq_lens"), rank, N, I, _i32(out, "out"),
                                  _stream(stream)), "cp_local_seq_lens")
     return out
@@ -96,9 +158,12 @@ def cp_slot_map(req, pos, block_table, rank: int, N: int, I: int, bs: int, max_b
     """Slot of every token on ``rank`` (int64 [T]; -1 not mine, -2 invalid)."""
     lib = _lib.load()
     T = req.numel()
+    _count(pos, T, "pos")
+    _block_table(block_table, 1)
     B, stride = block_table.shape
     if out is None:
         out = torch.empty(T, dtype=torch.int64, device=req.device)
+    _count(out, T, "out", torch.int64)
     mb = stride if max_blocks is None else max_blocks
     _check(lib.cp_slot_map(T, _i32(req, "req"), _i32(pos, "pos"),
                            _i32(block_table, "block_table"), B, stride, mb, rank, N, I, bs,
@@ -114,13 +179,8 @@ def cp_cache_write(slot, k, v, k_cache, v_cache, bs: int, stream=None):
     T = slot.numel()
     if slot.dtype != torch.int64:
         raise ValueError("slot must be int64")
-    if v is None:
-        heads, row = 1, k.shape[-1]
-    else:
-        heads, row = k.shape[1], k.shape[2]
+    heads, row = _rows_and_caches(T, k, v, k_cache, v_cache, bs)
     num_blocks = k_cache.shape[0]
-    if k.dtype != k_cache.dtype or (v is not None and v.dtype != v_cache.dtype):
-        raise ValueError("rows and cache must share a dtype")
     _check(lib.cp_cache_write(T, _ptr(slot), _ptr(k), _ptr(v), heads, row, _dt(k), _ptr(k_cache),
                               _ptr(v_cache), num_blocks, bs, _stream(stream)), "cp_cache_write")
 
@@ -131,16 +191,13 @@ def cp_slot_map_cache_write(req, pos, block_table, rank: int, N: int, I: int, bs
     go to ``slot_out`` (int64 [T]) when it is given."""
     lib = _lib.load()
     T = req.numel()
+    _count(pos, T, "pos")
+    _block_table(block_table, 1)
     B, stride = block_table.shape
     mb = stride if max_blocks is None else max_blocks
-    if v is None:
-        heads, row = 1, k.shape[-1]
-    else:
-        heads, row = k.shape[1], k.shape[2]
-    if k.dtype != k_cache.dtype or (v is not None and v.dtype != v_cache.dtype):
-        raise ValueError("rows and cache must share a dtype")
-    if slot_out is not None and slot_out.dtype != torch.int64:
-        raise ValueError("slot_out must be int64")
+    heads, row = _rows_and_caches(T, k, v, k_cache, v_cache, bs)
+    if slot_out is not None:
+        _count(slot_out, T, "slot_out", torch.int64)
     _check(lib.cp_slot_map_cache_write(T, _i32(req, "req"), _i32(pos, "pos"),
                                        _i32(block_table, "block_table"), B, stride, mb, rank, N, I,
                                        bs, _ptr(slot_out), _ptr(k), _ptr(v), heads, row, _dt(k),
@@ -153,11 +210,23 @@ def cp_slot_map_cache_write(req, pos, block_table, rank: int, N: int, I: int, bs
 # decode partials
 # ---------------------------------------------------------------------------
 
+def _gqa_common(q, k_cache, v_cache, block_table, local_len, B, Hq, D):
+    if k_cache is None or k_cache.dim() != 4:
+        raise ValueError("k_cache must be [num_blocks, Hkv, bs, D]")
+    _shape(k_cache, (None, None, None, D), "k_cache", q.dtype)
+    _shape(v_cache, tuple(k_cache.shape), "v_cache", q.dtype)
+    _block_table(block_table, B)
+    _count(local_len, B, "local_len")
+    return k_cache.shape
+
+
 def gqa_args(q, k_cache, v_cache, block_table, local_len, scale, out, lse):
+    if q.dim() != 3:
+        raise ValueError(f"q has shape {list(q.shape)}, expected [B, Hq, D]")
     B, Hq, D = q.shape
-    nb, Hkv, bs, D2 = k_cache.shape
-    if D2 != D or v_cache.shape != k_cache.shape:
-        raise ValueError("cache shape mismatch")
+    nb, Hkv, bs, _ = _gqa_common(q, k_cache, v_cache, block_table, local_len, B, Hq, D)
+    _shape(out, (B, Hq, D), "out", torch.float32)
+    _shape(lse, (B, Hq), "lse", torch.float32)
     return _lib.CpGqaArgs(q=_ptr(q), k_cache=_ptr(k_cache), v_cache=_ptr(v_cache),
                           block_table=_i32(block_table, "block_table"),
                           local_len=_i32(local_len, "local_len"), B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs,
@@ -166,10 +235,21 @@ def gqa_args(q, k_cache, v_cache, block_table, local_len, scale, out, lse):
 
 
 def mla_args(q, kv_cache, block_table, local_len, scale, out, lse, Dv=512, kv_scale=1.0):
+    if q.dim() != 3:
+        raise ValueError(f"q has shape {list(q.shape)}, expected [B, H, Dk]")
+    if q.dtype != torch.bfloat16:
+        raise ValueError(f"q has dtype {q.dtype}, expected torch.bfloat16")
     B, H, Dk = q.shape
-    nb, bs, Dk2 = kv_cache.shape
-    if Dk2 != Dk:
-        raise ValueError("latent width mismatch")
+    if kv_cache is None or kv_cache.dim() != 3:
+        raise ValueError("kv_cache must be [num_blocks, bs, Dk]")
+    _shape(kv_cache, (None, None, Dk), "kv_cache")
+    if kv_cache.dtype not in (torch.bfloat16, torch.float8_e4m3fn):
+        raise ValueError(f"kv_cache has dtype {kv_cache.dtype}, expected bf16 or fp8 e4m3fn")
+    nb, bs, _ = kv_cache.shape
+    _block_table(block_table, B)
+    _count(local_len, B, "local_len")
+    _shape(out, (B, H, Dv), "out", torch.float32)
+    _shape(lse, (B, H), "lse", torch.float32)
     return _lib.CpMlaArgs(q=_ptr(q), kv_cache=_ptr(kv_cache),
                           block_table=_i32(block_table, "block_table"),
                           local_len=_i32(local_len, "local_len"), B=B, H=H, Dk=Dk, Dv=Dv, bs=bs,
@@ -214,10 +294,13 @@ def gqa_mtp_args(q, k_cache, v_cache, block_table, local_len, seq_len, scale, ou
                  I):
     """Arguments of the multi-token entry; q [B][T][Hq][D], out [B][T][Hq][D],
     lse [B][T][Hq]."""
+    if q.dim() != 4:
+        raise ValueError(f"q has shape {list(q.shape)}, expected [B, T, Hq, D]")
     B, T, Hq, D = q.shape
-    nb, Hkv, bs, D2 = k_cache.shape
-    if D2 != D or v_cache.shape != k_cache.shape:
-        raise ValueError("cache shape mismatch")
+    nb, Hkv, bs, _ = _gqa_common(q, k_cache, v_cache, block_table, local_len, B, Hq, D)
+    _count(seq_len, B, "seq_len")
+    _shape(out, (B, T, Hq, D), "out", torch.float32)
+    _shape(lse, (B, T, Hq), "lse", torch.float32)
     base = _lib.CpGqaArgs(q=_ptr(q), k_cache=_ptr(k_cache), v_cache=_ptr(v_cache),
                           block_table=_i32(block_table, "block_table"),
                           local_len=_i32(local_len, "local_len"), B=B, Hq=Hq, Hkv=Hkv, D=D, bs=bs,
@@ -283,6 +366,9 @@ def cp_lse_merge(part_out, part_lse, out=None, lse_out=None, out_dtype=torch.flo
         out = torch.empty(part_out.shape[1:], dtype=out_dtype, device=part_out.device)
     if lse_out is None:
         lse_out = torch.empty(part_lse.shape[1:], dtype=torch.float32, device=part_out.device)
+    if out.numel() != rows * Dv or out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"out must hold rows x Dv = {rows * Dv} fp32 or bf16 elements")
+    _count(lse_out, rows, "lse_out", torch.float32)
     _check(lib.cp_lse_merge(n, rows, Dv, _ptr(part_out), _ptr(part_lse), _ptr(out), _dt(out),
                             _ptr(lse_out), _stream(stream)), "cp_lse_merge")
     return out, lse_out
@@ -303,6 +389,8 @@ def cp_lse_correct(part_out_i, part_lse, rank, corrected=None, lse_out=None, str
         corrected = torch.empty_like(part_out_i)
     if lse_out is None:
         lse_out = torch.empty(part_lse.shape[1:], dtype=torch.float32, device=part_lse.device)
+    _count(corrected, rows * Dv, "corrected", torch.float32)
+    _count(lse_out, rows, "lse_out", torch.float32)
     _check(lib.cp_lse_correct(n, rows, Dv, int(rank), _ptr(part_out_i), _ptr(part_lse),
                               _ptr(corrected), _ptr(lse_out), _stream(stream)), "cp_lse_correct")
     return corrected, lse_out
@@ -319,6 +407,7 @@ def cp_a2a_pack(out, lse, N, buf=None, stream=None):
         raise ValueError(f"H={H} is not a multiple of N={N}")
     if buf is None:
         buf = torch.empty((N, B, H // N, Dv + 4), dtype=torch.float32, device=out.device)
+    _shape(buf, (N, B, H // N, Dv + 4), "buf", torch.float32)
     _check(lib.cp_a2a_pack(B, H, Dv, N, _ptr(out), _ptr(lse), _ptr(buf), _stream(stream)),
            "cp_a2a_pack")
     return buf
@@ -345,6 +434,9 @@ def cp_lse_merge_packed(packed, Dv, out=None, lse_out=None, out_dtype=torch.floa
         out = torch.empty(lead + (Dv,), dtype=out_dtype, device=packed.device)
     if lse_out is None:
         lse_out = torch.empty(lead, dtype=torch.float32, device=packed.device)
+    if out.numel() != rows * Dv or out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"out must hold rows x Dv = {rows * Dv} fp32 or bf16 elements")
+    _count(lse_out, rows, "lse_out", torch.float32)
     _check(lib.cp_lse_merge_packed(n, rows, Dv, ctypes.c_void_p(packed.data_ptr()), stride, _ptr(out), _dt(out),
                                    _ptr(lse_out), _stream(stream)), "cp_lse_merge_packed")
     return out, lse_out
@@ -358,14 +450,35 @@ def prefill_args(q, P, pcp_rank, pcp_size, scale, out, lse, *, k=None, v=None, k
                  v_cache=None, block_table=None, local_len=0, dcp=None):
     """``dcp=(rank, size, interleave)`` selects the causal paged source (a DCP
     shard holding prefix and chunk keys)."""
+    if q.dim() != 3 or q.dtype != torch.bfloat16:
+        raise ValueError(f"q must be bf16 [C, Hq, D], got {q.dtype} {list(q.shape)}")
     C, Hq, D = q.shape
     dr, ds, di = dcp if dcp is not None else (0, 1, 1)
+    if (k is None) == (k_cache is None):
+        raise ValueError("give either the chunk's k, v (dense) or a paged k_cache, v_cache")
     if k is not None:
+        if k_cache is not None or v_cache is not None or block_table is not None or dcp:
+            raise ValueError("the dense source takes no paged arguments")
+        _shape(k, (C, None, D), "k", torch.bfloat16)
+        _shape(v, tuple(k.shape), "v", torch.bfloat16)
         src, Hkv = CP_KV_DENSE, k.shape[1]
         nb, bs, stride = 0, 16, 1
     else:
+        if k is not None or v is not None:
+            raise ValueError("the paged source takes no dense k, v")
+        if k_cache.dim() != 4:
+            raise ValueError("k_cache must be [num_blocks, Hkv, bs, D]")
+        _shape(k_cache, (None, None, None, D), "k_cache", torch.bfloat16)
+        _shape(v_cache, tuple(k_cache.shape), "v_cache", torch.bfloat16)
+        if block_table is None or block_table.dim() != 1 or block_table.dtype != torch.int32:
+            raise ValueError("block_table must be a 1-D int32 tensor (the shard's blocks)")
         src, Hkv = (CP_KV_PAGED if dcp is None else CP_KV_PAGED_CAUSAL), k_cache.shape[1]
         nb, bs, stride = k_cache.shape[0], k_cache.shape[2], block_table.numel()
+    if pcp_size < 1 or C % (2 * pcp_size):
+        raise ValueError(f"C={C} must be a multiple of 2 x pcp_size={pcp_size}")
+    c = C // (2 * pcp_size)
+    _shape(out, (2, c, Hq, D), "out", torch.float32)
+    _shape(lse, (2, c, Hq), "lse", torch.float32)
     return _lib.CpPrefillArgs(
         q=_ptr(q), C=C, P=P, pcp_rank=pcp_rank, pcp_size=pcp_size, Hq=Hq, Hkv=Hkv, D=D,
         scale=scale, kv_source=src, k=_ptr(k), v=_ptr(v), k_cache=_ptr(k_cache),
@@ -385,7 +498,7 @@ def pcp_prefill_attn_causal(q, P, pcp_rank, pcp_size, scale, *, k=None, v=None, 
     [2][C/2N][Hq][D], lse fp32 [2][C/2N][Hq])."""
     lib = _lib.load()
     C, Hq, D = q.shape
-    c = C // (2 * pcp_size)
+    c = C // (2 * pcp_size) if pcp_size >= 1 else 0
     if out is None:
         out = torch.empty(2, c, Hq, D, dtype=torch.float32, device=q.device)
     if lse is None:
@@ -408,7 +521,24 @@ def kv_gather_args(k_caches, v_caches, block_tables, seq_len, N: int, I: int, bs
     if len(k_caches) != N or len(block_tables) != N or (v_caches is not None and len(v_caches) != N):
         raise ValueError("one cache and one block table per shard")
     kc0 = k_caches[0]
+    if kc0.dim() not in (3, 4):
+        raise ValueError("caches must be [num_blocks, Hkv, bs, D] or [num_blocks, bs, D]")
     Hkv, D = (kc0.shape[1], kc0.shape[3]) if kc0.dim() == 4 else (1, kc0.shape[2])
+    B = int(seq_len.shape[0])
+    row = (None, Hkv, bs, D) if kc0.dim() == 4 else (None, bs, D)
+    for r in range(N):
+        _shape(k_caches[r], row, f"k_caches[{r}]", kc0.dtype)
+        if v_caches is not None:
+            _shape(v_caches[r], tuple(k_caches[r].shape), f"v_caches[{r}]", kc0.dtype)
+        _block_table(block_tables[r], B, f"block_tables[{r}]")
+        if block_tables[r].shape[1] != block_tables[0].shape[1]:
+            raise ValueError("every shard's block table must have the same width")
+    _count(seq_len, B, "seq_len")
+    _shape(k_out, (B, W, Hkv, D), "k_out", kc0.dtype)
+    if (v_out is None) != (v_caches is None):
+        raise ValueError("v_out must be given exactly when v_caches is")
+    if v_out is not None:
+        _shape(v_out, (B, W, Hkv, D), "v_out", kc0.dtype)
     arr = ctypes.c_void_p * N
     kp = arr(*[_ptr(c).value for c in k_caches])
     vp = arr(*[_ptr(c).value for c in v_caches]) if v_caches is not None else None

@@ -177,9 +177,15 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
     const int npieces = 2 * p.pcp_size;
     const int piece = piece_slot == 0 ? p.pcp_rank : npieces - 1 - p.pcp_rank;
     const int c = p.C / npieces;                    // rows per piece
+    const int pe = piece * c + c;                   // end of the piece (exclusive)
     const int i0 = piece * c + qb * kBM * p.R;      // first query row of the workgroup
     const int i0w = i0 + kBM * rb;                  // first query row of this wave
     const int h = g * p.G + hw;                     // this wave's query head
+    // A piece need not be a multiple of 32 rows: the last row block of a piece
+    // is partial, and a wave whose rows all lie past the piece's end (i0w >= pe)
+    // computes nothing but still stages its share of every tile.  Rows past the
+    // end read the piece's last row (in bounds) and are never written.
+    const bool wave_rows = i0w < pe;
 
     // keys staged for the workgroup (causal: [0, i0 + 32 R); paged shard:
     // [0, local_len)) and keys visible to this wave's rows
@@ -191,16 +197,16 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
         if (!p.dcp_causal) return p.local_len;
         return min(p.local_len, owned_below(p.P + i + 1, p.dcp_rank, p.dcp_size, p.dcp_I));
     };
-    const int32_t kend = row_keys(min(i0 + kBM * p.R, p.C) - 1);  // staged for the workgroup
-    const int32_t kend_w = row_keys(min(i0w + kBM, p.C) - 1);     // this wave's last row
-    const int32_t kfirst_w = row_keys(i0w);                      // this wave's first row
-    const int32_t klim_r = row_keys(min(i0w + r32, p.C - 1));    // this lane's row
+    const int32_t kend = row_keys(min(i0 + kBM * p.R, pe) - 1);   // staged for the workgroup
+    const int32_t kend_w = wave_rows ? row_keys(min(i0w + kBM, pe) - 1) : 0;  // wave's last row
+    const int32_t kfirst_w = row_keys(min(i0w, pe - 1));          // this wave's first row
+    const int32_t klim_r = row_keys(min(i0w + r32, pe - 1));      // this lane's row
     const int bs = 1 << p.bs_log2;
 
     // ---- queries as the B operand: lane l holds Q[i0w + l % 32][h][16 ks + 8 (l / 32) .. +8] ----
     u32x4_t qb_reg[8];
     {
-        gbyte *qrow = p.q + ((int64_t)(i0w + r32) * p.Hq + h) * (kD * 2) + hf * 16;
+        gbyte *qrow = p.q + ((int64_t)min(i0w + r32, pe - 1) * p.Hq + h) * (kD * 2) + hf * 16;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) qb_reg[ks] = load16(qrow + ks * 32);
     }
@@ -530,10 +536,12 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
         const float iv = __shfl(inv_r, acc_row(e, hf), 64);
         const int r = local0 + acc_row(e, hf);
         float *dst = p.out + (((int64_t)piece_slot * c + r) * p.Hq + h) * kD + r32;
+        if (r < c) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) dst[db * 32] = o[db][e] * iv;
+            for (int db = 0; db < 4; ++db) dst[db * 32] = o[db][e] * iv;
+        }
     }
-    if (lane < 32) {
+    if (lane < 32 && local0 + lane < c) {
         const int r = local0 + lane;
         p.lse[((int64_t)piece_slot * c + r) * p.Hq + h] =
             bad ? NAN : (m_ref == -INFINITY || !(lt > 0.f) ? -INFINITY : (m_ref + fast_log2(lt)) * kLn2);
@@ -572,9 +580,7 @@ extern "C" cp_status pcp_prefill_attn_causal(const cp_prefill_args *a, void *ws,
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(CP_E_UNSUPPORTED, "prefill: Hq/Hkv = %d not in {1, 2, 4, 8}", G);
     const int rows = a->C / (2 * a->pcp_size);
-    if (rows % kBM != 0)
-        return fail(CP_E_UNSUPPORTED, "prefill: piece of %d rows is not a multiple of %d", rows,
-                    kBM);
+    const int nrb = (rows + kBM - 1) / kBM;  // 32-row blocks per piece (the last may be partial)
     if (a->kv_source != CP_KV_DENSE && a->kv_source != CP_KV_PAGED &&
         a->kv_source != CP_KV_PAGED_CAUSAL)
         return fail(CP_E_INVALID, "prefill: kv_source %d", a->kv_source);
@@ -640,12 +646,16 @@ extern "C" cp_status pcp_prefill_attn_causal(const cp_prefill_args *a, void *ws,
     p.qk_scale = a->scale * kLog2e;
     // R row blocks per workgroup: eight waves where the piece's row blocks divide
     int R = 8 / G;
-    while (R > 1 && (rows / kBM) % R != 0) R /= 2;
+    while (R > 1 && nrb % R != 0) R /= 2;
+    // at least two waves: a lone wave would keep two tiles' 32 copies each in
+    // flight, past the 63 outstanding loads its counter can track (the second
+    // wave of a one-block piece has no rows and only stages)
+    if (G * R < 2) R = 2;
     int G_log2 = 0;
     while ((1 << G_log2) < G) ++G_log2;
     p.R = R;
     p.G_log2 = G_log2;
-    p.nqb = rows / (kBM * R);
+    p.nqb = (nrb + R - 1) / R;
     p.out = a->out;
     p.lse = a->lse;
     p.dcp_causal = dcp_causal ? 1 : 0;

@@ -6,8 +6,10 @@ sees only the generator's logical q/k/v, lengths, positions and block tables.
 """
 from __future__ import annotations
 
+import json
 import math
-from dataclasses import dataclass
+import os
+from dataclasses import dataclass, field
 
 import numpy as np
 import torch
@@ -27,38 +29,78 @@ def announce(msg: str):
 # tolerance gates
 # ---------------------------------------------------------------------------
 
-def gate_f32(got, ref, name):
-    """fp32 configs: |d| <= 1e-5 |ref| + 1e-6 max|ref| element-wise.
+GATE_LOG = os.environ.get("CP_GATE_LOG")  # optional JSONL file of every gate's margin
 
-    1e-5 relative is the stated fp32 tolerance; an element that is the result of
-    cancellation (a near-zero weighted sum of O(1) values) cannot be relative-
-    accurate, so the floor is the fp32 rounding level of the row's scale: a sum of
-    n ~ 10^2..10^4 rounded terms has error ~ sqrt(n) * 2^-24 * max|ref| <= 1e-6 max|ref|."""
+
+def _record(name, kind, dmax, scale, used):
+    """Print (and optionally log) a gate's achieved error: max|d|, max|d| / max|ref|
+    and the largest fraction of the element-wise bound used."""
+    ratio = dmax / scale if scale > 0 else 0.0
+    print(f"[gate] {kind} {name}: max|d| = {dmax:.3e}, max|d|/max|ref| = {ratio:.3e}, "
+          f"bound used {used:.3f}", flush=True)
+    if GATE_LOG:
+        with open(GATE_LOG, "a") as f:
+            f.write(json.dumps({"test": os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0],
+                                "gate": name, "kind": kind, "max_abs": dmax,
+                                "max_rel_to_max_ref": ratio, "bound_used": used}) + "\n")
+
+
+def _same_nonfinite(got, ref, name):
+    """Non-finite values must sit exactly where the oracle's are: -inf where the
+    oracle has -inf (empty key sets), NaN where it has NaN, and a finite value
+    everywhere else."""
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), f"{name}: -inf pattern differs"
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), f"{name}: NaN pattern differs"
+    fin = np.isfinite(ref)
+    assert np.isfinite(got[fin]).all(), f"{name}: non-finite values where the oracle is finite"
+    return fin
+
+
+FP32_FLOOR = 1e-6
+
+
+def gate_f32(got, ref, name):
+    """fp32 configs: |d| <= 1e-5 |ref| + 1e-6 max|ref| element-wise, after the
+    non-finite patterns agree.
+
+    1e-5 relative is the stated fp32 tolerance.  A relative bound is undefined at
+    cancellation points (an output element that is a near-zero weighted sum of
+    O(1) values), so the gate adds an absolute floor at the rounding level of the
+    whole tensor.  The kernels' fp32 results are weighted sums o = sum_t w_t v_t
+    (sum_t w_t = 1) whose longest chain of dependent roundings has k <= ~50 steps
+    (a 32-key chunk per lane, then at most ~8 split parts and N shard parts); in
+    the probabilistic rounding model the error is ~ sqrt(k) * 2^-24 * sum_t w_t |v_t|,
+    about 4e-7 * max|v|, and max|v| is at most ~3 max|ref| for these inputs.  The
+    floor 1e-6 max|ref| sits a few standard deviations of that model above it;
+    each gate prints the achieved max|d| / max|ref| so the margin is visible."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    fin = np.isfinite(ref)
-    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), f"{name}: -inf pattern differs"
+    fin = _same_nonfinite(got, ref, name)
     scale = np.abs(ref[fin]).max(initial=0.0)
     d = np.abs(got[fin] - ref[fin])
-    bound = 1e-5 * np.abs(ref[fin]) + 1e-6 * scale
+    bound = 1e-5 * np.abs(ref[fin]) + FP32_FLOOR * scale
     bad = d > bound
+    _record(name, "f32", float(d.max(initial=0.0)), float(scale),
+            float((d / np.maximum(bound, 1e-300)).max(initial=0.0)))
     assert not bad.any(), (f"{name}: {bad.sum()} elements beyond fp32 gate, max |d| = {d.max():.3e}"
                            f", max|ref| = {scale:.3e}")
 
 
 def gate_lowp(got, ref, name, atol, norm=1e-2):
-    """bf16 / fp8 configs: |d| <= atol element-wise and max|d| <= norm * max|ref|."""
+    """bf16 / fp8 configs: |d| <= atol element-wise and max|d| <= norm * max|ref|,
+    after the non-finite patterns agree."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), f"{name}: -inf pattern differs"
-    fin = np.isfinite(ref)
-    assert np.isfinite(got[fin]).all(), f"{name}: non-finite values where the oracle is finite"
+    fin = _same_nonfinite(got, ref, name)
     d = np.abs(got[fin] - ref[fin])
     scale = np.abs(ref[fin]).max(initial=0.0)
-    assert d.max(initial=0.0) <= atol, f"{name}: max |d| = {d.max():.3e} > {atol}"
+    dmax = float(d.max(initial=0.0))
+    bound = atol if norm is None or scale == 0 else min(atol, norm * scale)
+    _record(name, "lowp", dmax, float(scale), dmax / bound if bound > 0 else 0.0)
+    assert dmax <= atol, f"{name}: max |d| = {dmax:.3e} > {atol}"
     if norm is not None and scale > 0:
-        assert d.max(initial=0.0) <= norm * scale, (
-            f"{name}: max |d| = {d.max():.3e} > {norm} x max|ref| = {norm * scale:.3e}")
+        assert dmax <= norm * scale, (
+            f"{name}: max |d| = {dmax:.3e} > {norm} x max|ref| = {norm * scale:.3e}")
 
 
 def lowp_gate_passes(got, ref, atol, norm=1e-2):
@@ -83,6 +125,7 @@ class DecodeCase:
     v: torch.Tensor | None          # device [sumL][Hkv][D] (None for MLA)
     kv_scale: float
     shards: list                    # per rank: dict(bt, bt_dev, pool, kc, vc, ll, ll_dev, slots)
+    host: dict = field(default_factory=dict)  # request b -> its logical rows on the host
 
 
 def build_decode_case(w: ci.Workload, *, seq=None, pool_factor=2.0, check_slots=True,
@@ -199,15 +242,47 @@ def oracle_request(case: DecodeCase, b: int, shard=None, heads=None):
     w = case.w
     lo, hi = int(case.offs[b]), int(case.offs[b + 1])
     q = ci.bits(case.q[b:b + 1].cpu())
-    if w.kind == "mla_decode":
-        lat = ci.bits(case.k[lo:hi].cpu())
-        k = v = lat
-        dv = w.Dv
-    else:
-        k = ci.bits(case.k[lo:hi].cpu())
-        v = ci.bits(case.v[lo:hi].cpu())
-        dv = None
+    if b not in case.host:
+        case.host.clear()  # keep one request's rows (a 1M-token request is 600 MB)
+        if w.kind == "mla_decode":
+            lat = ci.bits(case.k[lo:hi].cpu())
+            case.host[b] = (lat, lat)
+        else:
+            case.host[b] = (ci.bits(case.k[lo:hi].cpu()), ci.bits(case.v[lo:hi].cpu()))
+    k, v = case.host[b]
+    dv = w.Dv if w.kind == "mla_decode" else None
     out, lse = oracle.attention(q, k, v, key_begin=0, key_end=hi - lo, scale=w.scale,
                                 q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, Dv=dv,
                                 kv_scale=case.kv_scale, shard=shard, heads=heads)
     return out[0], lse[0]
+
+
+def miswritten_shard(case: DecodeCase, r: int, I_bad: int, pool_factor=1.25):
+    """Shard r's cache as a rank would hold it had it written the context with
+    interleave I_bad instead of the case's I (stale cache metadata, "Where It
+    Breaks" in the code-reading page): (cache, v cache or None, block table,
+    local lengths), all on the device."""
+    w = case.w
+    mla = w.kind == "mla_decode"
+    seq = case.seq
+    total = int(case.offs[-1])
+    req = torch.from_numpy(np.repeat(np.arange(w.B, dtype=np.int32), seq)).to(DEV)
+    pos = torch.from_numpy(np.concatenate([np.arange(L, dtype=np.int32) for L in seq])).to(DEV)
+    ll = oracle.local_lens(seq, r, w.N, I_bad)
+    bt, pool = ci.block_tables((ll.astype(np.int64) + w.bs - 1) // w.bs, w.seed + 900 + r,
+                               pool_factor)
+    bt_dev = torch.from_numpy(bt).to(DEV)
+    tdt = ci.TORCH_DTYPE[w.kv_dtype]
+    if mla:
+        kc = ci.nan_fill_(torch.empty(pool, w.bs, w.D, dtype=tdt, device=DEV), w.kv_dtype)
+        vc = None
+    else:
+        kc = ci.nan_fill_(torch.empty(pool, w.Hkv, w.bs, w.D, dtype=tdt, device=DEV), w.kv_dtype)
+        vc = ci.nan_fill_(torch.empty_like(kc), w.kv_dtype)
+    slots = cp.cp_slot_map(req, pos, bt_dev, r, w.N, I_bad, w.bs)
+    if mla:
+        cp.cp_cache_write(slots, case.k.view(total, w.D), None, kc, None, w.bs)
+    else:
+        cp.cp_cache_write(slots, case.k, case.v, kc, vc, w.bs)
+    torch.cuda.synchronize()
+    return kc, vc, bt_dev, torch.from_numpy(ll).to(DEV)

@@ -9,8 +9,8 @@ import torch
 
 import cp_inputs as ci
 import kv_context_parallelism_amd as cp
-from _cases import (announce, build_decode_case, gate_lowp, lowp_gate_passes, oracle_request,
-                    run_partials)
+from _cases import (announce, build_decode_case, gate_lowp, lowp_gate_passes, miswritten_shard,
+                    oracle_request, run_partials)
 
 pytestmark = pytest.mark.gpu
 
@@ -88,11 +88,44 @@ def test_mla_bf16_peaked_full_size_sampled_and_negative_control():
 
 
 def test_mla_fp8_full_workload_sampled():
+    """The 4-request, 1M-token fp8 workload: every shard's partial of one request
+    and their 8-way merge against unsharded attention over all 1,048,576 keys,
+    on four heads; then stale cache metadata that the gate must catch."""
     w = ci.WORKLOADS["mla_decode_fp8"]
     announce(f"{w.name} full size (1M-token contexts), seed={w.seed}")
-    case = build_decode_case(w, pool_factor=1.25, check_cache=False, check_slots=False)
-    # shard partials of one request on two shards (131,072 keys each), four heads
-    _check(case, [2], [0, 6], heads=[0, 31, 64, 127], merged=False)
+    case = build_decode_case(w, pool_factor=1.25)
+    heads = [0, 31, 64, 127]
+    _check(case, [2], range(w.N), heads=heads, merged=True)
+    # stale metadata on shard 6: (i) sixteen block-table entries of request 2
+    # (1,024 of its 131,072 keys) pointing at request 3's blocks -- a single
+    # 64-key block moves the outputs by only ~4e-3 max|ref| at this length,
+    # below what the 1e-2 max|ref| gate can see; (ii) the shard's cache written
+    # with interleave I + 1
+    r, b = 6, 2
+    sh = case.shards[r]
+    ro, _ = oracle_request(case, b, shard=(w.N, w.I, r), heads=heads)
+    bt = sh["bt_dev"].clone()
+    bt[b, 100:116] = bt[b + 1, 100:116]
+    o, _ = cp.cp_decode_attn_partial_mla(case.q, sh["kc"], bt, sh["ll_dev"], w.scale, Dv=w.Dv,
+                                         kv_scale=case.kv_scale)
+    assert not lowp_gate_passes(o[b].cpu().numpy()[heads], ro, ATOL_OUT), "block-table control"
+    kc, _, bt_bad, ll_bad = miswritten_shard(case, r, w.I + 1)
+    o, _ = cp.cp_decode_attn_partial_mla(case.q, kc, bt_bad, ll_bad, w.scale, Dv=w.Dv,
+                                         kv_scale=case.kv_scale)
+    assert not lowp_gate_passes(o[b].cpu().numpy()[heads], ro, ATOL_OUT), "interleave control"
+
+
+def test_mla_bf16_peaked_interleave_control():
+    """Stale metadata on the peaked MLA twin: a shard whose cache was written
+    with interleave I + 1 must fail the gate."""
+    w = ci.scaled(ci.WORKLOADS["mla_decode_bf16_peaked"], B=4, seed=3500)
+    case = build_decode_case(w, seq=[9000, 12000, 4000, 8192], check_cache=False)
+    heads = [5, 77]
+    _check(case, [1], [2], heads=heads, merged=False)
+    kc, _, bt_bad, ll_bad = miswritten_shard(case, 2, w.I + 1)
+    o, _ = cp.cp_decode_attn_partial_mla(case.q, kc, bt_bad, ll_bad, w.scale, Dv=w.Dv)
+    ro, _ = oracle_request(case, 1, shard=(w.N, w.I, 2), heads=heads)
+    assert not lowp_gate_passes(o[1].cpu().numpy()[heads], ro, ATOL_OUT)
 
 
 def test_mla_unsupported_shapes():
