@@ -158,6 +158,23 @@ typedef struct cp_gqa_args {
 cp_status cp_decode_attn_partial_gqa(const cp_gqa_args *args, void *workspace,
                                      size_t workspace_bytes, hipStream_t stream);
 
+/* The same call without a caller workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses
+ * that forbid allocation): the split-context partials go to a scratch array
+ * the library holds on each device, of cp_noalloc_scratch_bytes() bytes
+ * (16 MiB; the array stays allocated on every GPU the library has run on
+ * until the process ends).  Results are those of cp_decode_attn_partial_gqa
+ * with a workspace.  The call allocates nothing.  All calls on one device
+ * share that device's array: calls that overlap in time on one device (other
+ * streams, other host threads) race and must be serialised by the caller.
+ * Errors: as cp_decode_attn_partial_gqa; CP_E_WORKSPACE if the call needs more
+ * split-partial space than the scratch holds (cp_workspace_bytes(
+ * CP_OP_DECODE_GQA, args) > cp_noalloc_scratch_bytes(), e.g. B x Hkv above
+ * ~7,000 at Hq/Hkv = 4, D = 128); CP_E_HIP if the scratch address cannot be
+ * looked up. */
+cp_status cp_decode_attn_partial_gqa_noalloc(const cp_gqa_args *args, hipStream_t stream);
+size_t cp_noalloc_scratch_bytes(void);
+
 /* Multi-token decode queries (speculative decoding / MTP verification: [P1]
  * "Inapplicable scenarios and known limitations" and [P4] "Future Roadmap"
  * name the combination of DCP with MTP and speculative decoding).  Request b's

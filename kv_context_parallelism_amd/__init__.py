@@ -22,7 +22,7 @@ from ._lib import (CP_BF16, CP_E_HIP, CP_E_INVALID, CP_E_UNSUPPORTED, CP_E_WORKS
 
 __all__ = [
     "CpError", "cp_local_seq_lens", "cp_slot_map", "cp_cache_write", "cp_decode_attn_partial_gqa",
-    "cp_decode_attn_partial_gqa_mtp", "gqa_mtp_args",
+    "cp_decode_attn_partial_gqa_mtp", "gqa_mtp_args", "cp_decode_attn_partial_gqa_noalloc",
     "cp_decode_attn_partial_mla", "cp_lse_merge", "cp_lse_correct", "cp_a2a_pack",
     "cp_lse_merge_packed", "pcp_prefill_attn_causal", "cp_workspace_bytes",
     "gqa_args", "mla_args", "prefill_args", "library_path", "cp_kv_gather", "kv_gather_args",
@@ -287,6 +287,19 @@ def cp_decode_attn_partial_gqa(q, k_cache, v_cache, block_table, local_len, scal
     ws, nws = _workspace(CP_OP_DECODE_GQA, a, q.device, workspace)
     _check(lib.cp_decode_attn_partial_gqa(ctypes.byref(a), _ptr(ws), nws, _stream(stream)),
            "cp_decode_attn_partial_gqa")
+    return out, lse
+
+
+def cp_decode_attn_partial_gqa_noalloc(q, k_cache, v_cache, block_table, local_len, scale, out,
+                                       lse, stream=None):
+    """cp_decode_attn_partial_gqa without a workspace: the split partials use the
+    library's per-device scratch, so nothing is allocated -- the caller passes
+    out (fp32 [B][Hq][D]) and lse (fp32 [B][Hq]).  Calls that overlap on one
+    device race on that scratch."""
+    lib = _lib.load()
+    a = gqa_args(q, k_cache, v_cache, block_table, local_len, scale, out, lse)
+    _check(lib.cp_decode_attn_partial_gqa_noalloc(ctypes.byref(a), _stream(stream)),
+           "cp_decode_attn_partial_gqa_noalloc")
     return out, lse
 
 

@@ -66,6 +66,8 @@ SIGNATURES = {
                                        _i32, _vp, _vp, _vp, _i32, _i32, _int, _vp, _vp, _i64,
                                        _vp]),
     "cp_decode_attn_partial_gqa": (_int, [ctypes.POINTER(CpGqaArgs), _vp, ctypes.c_size_t, _vp]),
+    "cp_decode_attn_partial_gqa_noalloc": (_int, [ctypes.POINTER(CpGqaArgs), _vp]),
+    "cp_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "cp_decode_attn_partial_gqa_mtp": (_int, [ctypes.POINTER(CpGqaMtpArgs), _vp, ctypes.c_size_t,
                                               _vp]),
     "cp_decode_attn_partial_mla": (_int, [ctypes.POINTER(CpMlaArgs), _vp, ctypes.c_size_t, _vp]),

@@ -446,7 +446,6 @@ GqaPlan plan_gqa(const cp_gqa_args &a) {
 using namespace cpattn;
 
 namespace cpattn {
-namespace {
 
 // Host checks shared by the single- and multi-token entries (CP_OK or the error).
 cp_status validate_gqa(const cp_gqa_args *a) {
@@ -473,6 +472,8 @@ cp_status validate_gqa(const cp_gqa_args *a) {
         return fail(CP_E_INVALID, "gqa decode: q, caches and out must be 16-byte aligned");
     return CP_OK;
 }
+
+namespace {
 
 // The row-layout kernel and its split combine: T x Hq/Hkv rows per KV head,
 // merged into out [B][T][Hq][D] and lse [B][T][Hq].

@@ -39,6 +39,8 @@ struct GqaPlan {
     size_t ws_bytes;       // partial outputs + LSEs (+ segment table), 0 if none
 };
 GqaPlan plan_gqa(const cp_gqa_args &a);
+// Host checks of a GQA decode call (CP_OK, or the error with its message set).
+cp_status validate_gqa(const cp_gqa_args *a);
 GqaPlan plan_gqa_mtp(const cp_gqa_mtp_args &m);
 
 struct MlaPlan {
