@@ -197,41 +197,53 @@ class GqaDecodeBench:
         if ev is not None:
             ev[w.N][1].record()
 
-    def cpu_baseline(self, budget_s=15.0):
+    def cpu_baseline(self, budget_s=15.0, min_s=1.0):
         """The fp64 oracle on the same workload: all shard partials of whole
-        requests plus their merge, request by request until the time budget is
-        spent.  Returns (KV GB/s, sample description)."""
+        requests plus their merge, request after request (cycling through the
+        batch again while less than ``min_s`` has passed) until the time budget
+        is spent.  Returns (KV GB/s, sample description)."""
         import numpy as np
 
         import cp_inputs as ci
         import oracle
 
         w = self.w
-        done, kv_bytes, t0 = 0, 0, time.perf_counter()
+        done, kv_bytes, passes, t0 = 0, 0, 0, time.perf_counter()
         q = ci.bits(self.q.cpu())
-        for b in range(w.B):
-            lo, hi = int(self.offs[b]), int(self.offs[b + 1])
-            k = ci.bits(self.k[lo:hi].cpu())
-            v = ci.bits(self.v[lo:hi].cpu())
-            po, pl = [], []
-            for r in range(w.N):
-                if self.T == 1:
-                    o, l = oracle.attention(q[b:b + 1], k, v, key_begin=0, key_end=hi - lo,
-                                            scale=w.scale, q_dtype=w.q_dtype,
-                                            kv_dtype=w.kv_dtype, shard=(w.N, w.I, r))
-                else:
-                    o, l = oracle.decode_mtp(q[b], k, v, L=hi - lo, scale=w.scale,
-                                             q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
-                                             shard=(w.N, w.I, r))
-                po.append(o.reshape(-1, w.D))
-                pl.append(l.reshape(-1))
-            oracle.lse_merge(np.stack(po), np.stack(pl))
-            done += 1
-            kv_bytes += (hi - lo) * w.Hkv * w.D * 2 * 2
-            if time.perf_counter() - t0 > budget_s:
-                break
+        host = {}
+        over = False
+        while not over:
+            for b in range(w.B):
+                lo, hi = int(self.offs[b]), int(self.offs[b + 1])
+                if b not in host:
+                    host[b] = (ci.bits(self.k[lo:hi].cpu()), ci.bits(self.v[lo:hi].cpu()))
+                k, v = host[b]
+                po, pl = [], []
+                for r in range(w.N):
+                    if self.T == 1:
+                        o, l = oracle.attention(q[b:b + 1], k, v, key_begin=0, key_end=hi - lo,
+                                                scale=w.scale, q_dtype=w.q_dtype,
+                                                kv_dtype=w.kv_dtype, shard=(w.N, w.I, r))
+                    else:
+                        o, l = oracle.decode_mtp(q[b], k, v, L=hi - lo, scale=w.scale,
+                                                 q_dtype=w.q_dtype, kv_dtype=w.kv_dtype,
+                                                 shard=(w.N, w.I, r))
+                    po.append(o.reshape(-1, w.D))
+                    pl.append(l.reshape(-1))
+                oracle.lse_merge(np.stack(po), np.stack(pl))
+                done += 1
+                kv_bytes += (hi - lo) * w.Hkv * w.D * self.q.element_size() * 2
+                if time.perf_counter() - t0 > budget_s:
+                    over = True
+                    break
+            else:
+                passes += 1
+                over = over or time.perf_counter() - t0 >= min_s
         dt = time.perf_counter() - t0
-        return kv_bytes / dt / 1e9, f"{done} of {w.B} requests (all {w.N} shard partials + merge)"
+        self.cpu_step_s = dt / done * w.B  # one whole step of the batch
+        return kv_bytes / dt / 1e9, (f"{done} request partial sets ({passes} whole passes over "
+                                     f"the {w.B} requests; each: all {w.N} shard partials + "
+                                     "merge)")
 
     def config(self):
         w = self.w
@@ -415,10 +427,11 @@ class PrefillBench:
             self.shards.append(dict(ll=ll, bt_d=bt_d, bt_row=bt_d[0].contiguous(), kc=kc, vc=vc,
                                     slots=torch.empty(C, dtype=torch.int64, device=dev)))
         c = C // (2 * w.N)
-        self.part_out = torch.empty(w.N + 1, 2 * c, w.Hq, w.D, dtype=torch.float32, device=dev)
-        self.part_lse = torch.empty(w.N + 1, 2 * c, w.Hq, dtype=torch.float32, device=dev)
-        self.out = torch.empty(w.N, 2 * c, w.Hq, w.D, dtype=torch.float32, device=dev)
-        self.lse = torch.empty(w.N, 2 * c, w.Hq, dtype=torch.float32, device=dev)
+        # per rank: the two pieces [2][c] of its causal-chunk and prefix-shard partials
+        self.part_out = torch.empty(w.N + 1, 2, c, w.Hq, w.D, dtype=torch.float32, device=dev)
+        self.part_lse = torch.empty(w.N + 1, 2, c, w.Hq, dtype=torch.float32, device=dev)
+        self.out = torch.empty(w.N, 2, c, w.Hq, w.D, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(w.N, 2, c, w.Hq, dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
         causal = C * (C + 1) // 2
         self.work_causal = causal * w.Hq * 4 * w.D
@@ -533,10 +546,10 @@ class DcpPrefillBench:
             self.shards.append(dict(ll=ll, bt_d=bt_d, bt_row=bt_d[0].contiguous(), kc=kc, vc=vc,
                                     slots=torch.empty(C, dtype=torch.int64, device=dev)))
         c = C // (2 * w.N)
-        self.part_out = torch.empty(w.N, 2 * c, w.Hq, w.D, dtype=torch.float32, device=dev)
-        self.part_lse = torch.empty(w.N, 2 * c, w.Hq, dtype=torch.float32, device=dev)
-        self.out = torch.empty(w.N, 2 * c, w.Hq, w.D, dtype=torch.float32, device=dev)
-        self.lse = torch.empty(w.N, 2 * c, w.Hq, dtype=torch.float32, device=dev)
+        self.part_out = torch.empty(w.N, 2, c, w.Hq, w.D, dtype=torch.float32, device=dev)
+        self.part_lse = torch.empty(w.N, 2, c, w.Hq, dtype=torch.float32, device=dev)
+        self.out = torch.empty(w.N, 2, c, w.Hq, w.D, dtype=torch.float32, device=dev)
+        self.lse = torch.empty(w.N, 2, c, w.Hq, dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
         causal = C * (C + 1) // 2
         # every (query, key) pair with key position <= query position, once
@@ -807,6 +820,162 @@ BENCH_WORKLOADS = ["gqa_decode_bf16", "gqa_decode_mtp_bf16", "mla_decode_bf16", 
                    "pcp_prefill_bf16", "dcp_prefill_bf16", "kv_gather_bf16", "head_scatter_mla"]
 
 
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def measure(bench, steps: int, warmup: int) -> dict:
+    """Warm up, then time exactly ``steps`` steps of ``bench`` with HIP events
+    around every launch of interest and around every step; returns the fields
+    of a bench line (value, step times, the dominant kernel's roofline, the
+    final merge)."""
+    import torch
+
+    w = bench.w
+    for _ in range(warmup):
+        bench.step()
+    torch.cuda.synchronize()
+    n_ev = bench.launches_per_step
+    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))  # noqa
+    ev = [[mk() for _ in range(n_ev)] for _ in range(steps)]
+    sev = [mk() for _ in range(steps)]
+    print(f"[bench] {w.name}: timing {steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        sev[i][0].record()
+        bench.step(ev[i])
+        sev[i][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / steps
+    step_ms = [a.elapsed_time(b) for a, b in sev]
+    per_event = getattr(bench, "launches_per_event", 1)  # launches between one event pair
+    launch_ms = [step[k][0].elapsed_time(step[k][1]) / per_event for step in ev
+                 for k in bench.dominant]
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    med_launch_s = _median(launch_ms) / 1e3
+    unit = bench.metric_unit
+    if unit == "GB/s":
+        scale_v, peak, bound = 1e9, HBM_PEAK_GBS, "hbm"
+    else:
+        scale_v, peak, bound = 1e12, BF16_PEAK_TFLOPS, "mfma"
+    avg_work = sum(bench.per_launch_work) / len(bench.per_launch_work)
+    achieved = avg_work / avg_launch_s / scale_v
+    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": _counted_traffic(w.name),
+            "kernel": bench.kernel_name,
+            "avg_launch_us": round(avg_launch_s * 1e6, 2),
+            "median_launch_us": round(med_launch_s * 1e6, 2),
+            "launches_timed": len(launch_ms),
+            ("algorithmic_bytes_per_launch" if unit == "GB/s" else "algorithmic_flop_per_launch"):
+                int(avg_work)}
+    if unit != "GB/s":
+        avg_bytes = sum(bench.per_launch_bytes) / len(bench.per_launch_bytes)
+        roof["hbm_gbs"] = round(avg_bytes / avg_launch_s / 1e9, 2) if avg_bytes else None
+    if getattr(bench, "secondary", None):
+        sec_ms = [step[k][0].elapsed_time(step[k][1]) for step in ev for k in bench.secondary]
+        sec_s = sum(sec_ms) / len(sec_ms) / 1e3
+        roof["secondary"] = {"kernel": "pcp_prefill_attn_causal over the chunk's own keys",
+                             "avg_launch_us": round(sec_s * 1e6, 2),
+                             "median_launch_us": round(_median(sec_ms) * 1e3, 2),
+                             "achieved": round(bench.secondary_work / sec_s / scale_v, 2),
+                             "frac": round(bench.secondary_work / sec_s / scale_v / peak, 4)}
+    if getattr(bench, "secondaries", None):
+        roof["secondary"] = []
+        for name, idx, work in bench.secondaries:
+            sec_ms = [step[k][0].elapsed_time(step[k][1]) / per_event for step in ev for k in idx]
+            sec_s = sum(sec_ms) / len(sec_ms) / 1e3
+            roof["secondary"].append({"kernel": name, "avg_launch_us": round(sec_s * 1e6, 2),
+                                      "median_launch_us": round(_median(sec_ms) * 1e3, 2),
+                                      "achieved": round(work / sec_s / scale_v, 2),
+                                      "frac": round(work / sec_s / scale_v / peak, 4)})
+    out = {"value": round(bench.work_step / (ms_step / 1e3) / scale_v, 2), "unit": unit,
+           "ms_per_step": round(ms_step, 4), "median_step_ms": round(_median(step_ms), 4),
+           "roofline": roof}
+    if getattr(bench, "merge_idx", None) is not None:
+        m_ms = [step[bench.merge_idx][0].elapsed_time(step[bench.merge_idx][1]) for step in ev]
+        m_s = sum(m_ms) / len(m_ms) / 1e3
+        out["merge"] = {"kernel": "cp_lse_merge of the N shard partials",
+                        "avg_launch_us": round(m_s * 1e6, 2),
+                        "median_launch_us": round(_median(m_ms) * 1e3, 2),
+                        "gbs": round(bench.merge_bytes / m_s / 1e9, 2)}
+    if getattr(bench, "tokens_step", None):
+        # tokens of one layer of the whole (simulated) CP group per second: the
+        # N ranks' calls run one after another on this GPU
+        out["tokens_per_s"] = round(bench.tokens_step / (ms_step / 1e3), 1)
+    return out
+
+
+def cpu_leg(bench, budget_s: float, one_thread: bool = False) -> dict:
+    """The untuned fp64 oracle on a bounded sample of the same workload, on
+    every host core this process may use (and, if asked, on one thread)."""
+    import oracle
+
+    cores = _cpu_cores()
+    oracle.set_threads(cores)
+    v, sample = bench.cpu_baseline(budget_s)
+    leg = {"value": round(v, 6), "unit": bench.metric_unit, "cores": cores, "kind": "oracle",
+           "sample": sample}
+    if hasattr(bench, "cpu_step_s"):
+        leg["step_ms"] = round(bench.cpu_step_s * 1e3, 3)
+    if one_thread:
+        oracle.set_threads(1)
+        v1, sample1 = bench.cpu_baseline(budget_s)
+        leg["one_thread"] = {"value": round(v1, 6), "unit": bench.metric_unit, "cores": 1,
+                             "sample": sample1}
+        if hasattr(bench, "cpu_step_s"):
+            leg["one_thread"]["step_ms"] = round(bench.cpu_step_s * 1e3, 3)
+        oracle.set_threads(cores)
+    return leg
+
+
+# The default run adds these to the headline line: the small fp32 case as a
+# latency, and the MLA (bf16, fp8) and prefill workloads with their own roofline
+# (TFLOP/s against the bf16 MFMA peak) and oracle timings.
+EXTRA_WORKLOADS = ["gqa_tiny_f32", "mla_decode_bf16", "mla_decode_fp8", "pcp_prefill_bf16"]
+
+
+def extra_block(name: str, steps: int, warmup: int, cpu: bool, budget_s: float) -> dict:
+    import torch
+
+    import cp_inputs as ci
+
+    w = ci.WORKLOADS[name]
+    print(f"[bench] setting up {w.name}", file=sys.stderr, flush=True)
+    bench = BENCHES[w.kind](w)
+    m = measure(bench, steps, warmup)
+    if name == "gqa_tiny_f32":
+        # a latency case: one decode step of 4 shards of a 1,000-token request
+        # (slot map + cache write, 4 shard partials, merge) in microseconds
+        block = {"metric": "step latency", "unit": "us", "higher_is_better": False,
+                 "latency_us_median": round(m["median_step_ms"] * 1e3, 2),
+                 "latency_us_mean": round(m["ms_per_step"] * 1e3, 2),
+                 "dtype": bench.dtype, "config": bench.config(),
+                 "shard_partial_median_us": m["roofline"]["median_launch_us"]}
+        if "merge" in m:
+            block["merge_median_us"] = m["merge"]["median_launch_us"]
+    else:
+        block = dict(m)
+        block["dtype"] = bench.dtype
+        block["config"] = bench.config()
+    if cpu:
+        print(f"[bench] {w.name}: timing the fp64 oracle", file=sys.stderr, flush=True)
+        leg = cpu_leg(bench, budget_s, one_thread=(name == "gqa_tiny_f32"))
+        if name == "gqa_tiny_f32":
+            leg = {"step_us": round(bench.cpu_step_s * 1e6, 1), "unit": "us", "cores": leg["cores"],
+                   "kind": "oracle", "sample": leg["sample"],
+                   "one_thread": {"step_us": round(leg["one_thread"]["step_ms"] * 1e3, 1),
+                                  "unit": "us", "cores": 1}}
+        block["cpu_baseline"] = leg
+    del bench
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return block
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -814,6 +983,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa_decode_bf16", choices=BENCH_WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="only the selected workload (the default run also measures "
+                         + ", ".join(EXTRA_WORKLOADS) + ")")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of a workload, run a plain device copy of MIB MiB (the "
                          "known-size reference that scales the HBM byte counters)")
@@ -841,78 +1013,29 @@ def main():
     w = ci.WORKLOADS[args.workload]
     print(f"[bench] setting up {w.name}", file=sys.stderr, flush=True)
     bench = BENCHES[w.kind](w)
-    for _ in range(args.warmup):
-        bench.step()
-    torch.cuda.synchronize()
-    n_ev = bench.launches_per_step
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n_ev)] for _ in range(args.steps)]
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        bench.step(ev[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_step = elapsed * 1e3 / args.steps
-    launch_ms = [step[k][0].elapsed_time(step[k][1]) for step in ev for k in bench.dominant]
-    per_event = getattr(bench, "launches_per_event", 1)  # launches between one event pair
-    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3 / per_event
-    unit = bench.metric_unit
-    if unit == "GB/s":
-        scale_v, peak, bound = 1e9, HBM_PEAK_GBS, "hbm"
-    else:
-        scale_v, peak, bound = 1e12, BF16_PEAK_TFLOPS, "mfma"
-    avg_work = sum(bench.per_launch_work) / len(bench.per_launch_work)
-    achieved = avg_work / avg_launch_s / scale_v
-    value = bench.work_step / (ms_step / 1e3) / scale_v
-    roof = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": _counted_traffic(w.name),
-            "kernel": bench.kernel_name,
-            "avg_launch_us": round(avg_launch_s * 1e6, 2),
-            ("algorithmic_bytes_per_launch" if unit == "GB/s" else "algorithmic_flop_per_launch"):
-                int(avg_work)}
-    if unit != "GB/s":
-        avg_bytes = sum(bench.per_launch_bytes) / len(bench.per_launch_bytes)
-        roof["hbm_gbs"] = round(avg_bytes / avg_launch_s / 1e9, 2) if avg_bytes else None
-    if getattr(bench, "secondary", None):
-        sec_ms = [step[k][0].elapsed_time(step[k][1]) for step in ev for k in bench.secondary]
-        sec_s = sum(sec_ms) / len(sec_ms) / 1e3
-        roof["secondary"] = {"kernel": "pcp_prefill_attn_causal over the chunk's own keys",
-                             "avg_launch_us": round(sec_s * 1e6, 2),
-                             "achieved": round(bench.secondary_work / sec_s / scale_v, 2),
-                             "frac": round(bench.secondary_work / sec_s / scale_v / peak, 4)}
-    if getattr(bench, "secondaries", None):
-        roof["secondary"] = []
-        for name, idx, work in bench.secondaries:
-            sec_ms = [step[k][0].elapsed_time(step[k][1]) for step in ev for k in idx]
-            sec_s = sum(sec_ms) / len(sec_ms) / 1e3 / per_event
-            roof["secondary"].append({"kernel": name, "avg_launch_us": round(sec_s * 1e6, 2),
-                                      "achieved": round(work / sec_s / scale_v, 2),
-                                      "frac": round(work / sec_s / scale_v / peak, 4)})
-    merge = None
-    if getattr(bench, "merge_idx", None) is not None:
-        m_ms = [step[bench.merge_idx][0].elapsed_time(step[bench.merge_idx][1]) for step in ev]
-        m_s = sum(m_ms) / len(m_ms) / 1e3
-        merge = {"kernel": "cp_lse_merge of the N shard partials", "avg_launch_us": round(m_s * 1e6, 2),
-                 "gbs": round(bench.merge_bytes / m_s / 1e9, 2)}
+    m = measure(bench, args.steps, args.warmup)
     line = {
-        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": bench.dtype,
-        "data": "synthetic", "config": bench.config(), "roofline": roof,
+        "metric": METRIC, "value": m["value"], "unit": m["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": m["ms_per_step"],
+        "median_step_ms": m["median_step_ms"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": bench.dtype, "data": "synthetic", "config": bench.config(),
+        "roofline": m["roofline"],
     }
-    if merge is not None:
-        line["merge"] = merge
-    if getattr(bench, "tokens_step", None):
-        # tokens of one layer of the whole (simulated) CP group per second: the
-        # N ranks' calls run one after another on this GPU
-        line["tokens_per_s"] = round(bench.tokens_step / (ms_step / 1e3), 1)
+    for key in ("merge", "tokens_per_s"):
+        if key in m:
+            line[key] = m[key]
     if not args.no_cpu_baseline:
         print("[bench] timing the fp64 oracle on a bounded sample", file=sys.stderr, flush=True)
-        v, sample = bench.cpu_baseline()
-        line["cpu_baseline"] = {"value": round(v, 6), "unit": unit, "cores": _cpu_cores(),
-                                "kind": "oracle", "sample": sample}
+        line["cpu_baseline"] = cpu_leg(bench, 15.0,
+                                       one_thread=args.workload == "gqa_decode_bf16")
+    del bench
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if args.workload == "gqa_decode_bf16" and not args.no_extra:
+        line["workloads"] = {}
+        for name in EXTRA_WORKLOADS:
+            line["workloads"][name] = extra_block(name, args.steps, args.warmup,
+                                                  not args.no_cpu_baseline, 10.0)
     print(json.dumps(line), flush=True)
 
 

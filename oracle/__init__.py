@@ -65,10 +65,24 @@ def _load():
         i64p, i64p,                         # key_begin key_end
         i64, i64, i64,                      # shard N I r
         ctypes.c_double, dp, dp]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_max_threads.argtypes = []
     lib.oracle_lse_merge.restype = None
     lib.oracle_lse_merge.argtypes = [i64, i64, i64, dp, dp, dp, dp]
     _lib = lib
     return lib
+
+
+def set_threads(n: int) -> None:
+    """Threads the oracle's parallel loops use from now on (timing only: the
+    results are the same for every thread count)."""
+    _load().oracle_set_threads(int(n))
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
 
 
 def _ptr(a, ctype):

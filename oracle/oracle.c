@@ -21,6 +21,7 @@
  * closed forms, invariants and torch's fp64 scaled_dot_product_attention.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -262,3 +263,9 @@ void oracle_lse_merge(int64_t n_parts, int64_t rows, int64_t Dv, const double *p
         lse[r] = l + log(asum);
     }
 }
+
+/* Threads of the OpenMP loops above (for timing the oracle at a stated core
+ * count; the results do not depend on it: every (query row, head) is computed
+ * by one thread in the same order). */
+void oracle_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int oracle_max_threads(void) { return omp_get_max_threads(); }
