@@ -226,10 +226,13 @@ typedef struct cp_mla_args {
  * per token shared by all H query heads ([P1] section 3 "MLA path", KV head
  * effectively 1; [P3] Deep Dive 6: local attention then exact merge).
  * Supported: Dk = 576, Dv = 512, bs a power of two >= 16, H a multiple of 16 up to
- * 128 (CP_E_UNSUPPORTED otherwise).
+ * 128, B up to 4096 (CP_E_UNSUPPORTED otherwise).
  * Bad lengths / block ids give NaN rows as for GQA.
- * Workspace: cp_workspace_bytes(CP_OP_DECODE_MLA, &args).
- * Errors: as cp_decode_attn_partial_gqa. */
+ * Workspace: cp_workspace_bytes(CP_OP_DECODE_MLA, &args); need not be
+ * initialised.
+ * Errors: as cp_decode_attn_partial_gqa, plus CP_E_INVALID for num_blocks < 1,
+ * a scale that is not finite, or (fp8) a kv_scale that is not positive and
+ * finite. */
 cp_status cp_decode_attn_partial_mla(const cp_mla_args *args, void *workspace,
                                      size_t workspace_bytes, hipStream_t stream);
 

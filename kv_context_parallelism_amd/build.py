@@ -30,12 +30,13 @@ CFLAGS = [
     "-I", INCLUDE, "-I", CSRC,
 ]
 
-# Per-file additions.  decode_mla.hip, prefill.hip: every accumulator of the kernel
-# (outputs, scores) must stay in arch VGPRs, where the online-softmax rescale
-# can update them in place; the default heuristic puts MFMA accumulators in
-# AGPRs and then copies all of them to VGPRs and back on every tile.
+# Per-file additions.  prefill.hip: every accumulator of the kernel (outputs,
+# scores) must stay in arch VGPRs, where the online-softmax rescale can update
+# them in place; the default heuristic puts MFMA accumulators in AGPRs and then
+# copies all of them to VGPRs and back on every tile.  (decode_mla.hip issues
+# its MFMAs from asm with explicit register classes -- output accumulators in
+# AGPRs, score accumulators in VGPRs -- and keeps the default.)
 FILE_FLAGS = {
-    "decode_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
