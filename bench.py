@@ -826,11 +826,66 @@ def _median(xs):
     return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
 
 
+def _step_outputs(bench) -> list:
+    """The tensors a step writes last (the merged output and LSE)."""
+    ts = []
+    for t in (getattr(bench, "out", None), getattr(bench, "lse", None)):
+        if isinstance(t, (list, tuple)):
+            ts.extend(t)
+        elif t is not None:
+            ts.append(t)
+    return ts
+
+
+def time_graph(bench, steps: int, warmup: int):
+    """The step captured once as a HIP graph (every launch of the step, the same
+    work as the eager step) and replayed: ``warmup`` untimed replays, then
+    exactly ``steps`` timed ones between synchronisations.  The outputs of the
+    last replay must equal the eager step's byte for byte.  Returns
+    (ms per step, median ms per step from events around each replay)."""
+    import torch
+
+    bench.step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in _step_outputs(bench)]
+    side = torch.cuda.Stream()  # capture needs the step warmed on a side stream
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        bench.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        bench.step()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    for t in _step_outputs(bench):
+        t.fill_(float("nan"))
+    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))  # noqa
+    sev = [mk() for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        sev[i][0].record()
+        g.replay()
+        sev[i][1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    for a, b in zip(ref, _step_outputs(bench)):
+        if not torch.equal(a.view(torch.uint8), b.view(torch.uint8)):
+            raise RuntimeError("graph replay of the step differs from the eager step")
+    del g
+    return elapsed * 1e3 / steps, _median([a.elapsed_time(b) for a, b in sev])
+
+
 def measure(bench, steps: int, warmup: int) -> dict:
     """Warm up, then time exactly ``steps`` steps of ``bench`` with HIP events
-    around every launch of interest and around every step; returns the fields
-    of a bench line (value, step times, the dominant kernel's roofline, the
-    final merge)."""
+    around every launch of interest and around every step (the launches'
+    roofline), and exactly ``steps`` replays of the step captured as a HIP
+    graph (the step rate); returns the fields of a bench line (value, step
+    times, the dominant kernel's roofline, the final merge)."""
     import torch
 
     w = bench.w
@@ -850,8 +905,8 @@ def measure(bench, steps: int, warmup: int) -> dict:
         sev[i][1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_step = elapsed * 1e3 / steps
-    step_ms = [a.elapsed_time(b) for a, b in sev]
+    eager_ms_step = elapsed * 1e3 / steps
+    eager_step_ms = [a.elapsed_time(b) for a, b in sev]
     per_event = getattr(bench, "launches_per_event", 1)  # launches between one event pair
     launch_ms = [step[k][0].elapsed_time(step[k][1]) / per_event for step in ev
                  for k in bench.dominant]
@@ -892,8 +947,16 @@ def measure(bench, steps: int, warmup: int) -> dict:
                                       "median_launch_us": round(_median(sec_ms) * 1e3, 2),
                                       "achieved": round(work / sec_s / scale_v, 2),
                                       "frac": round(work / sec_s / scale_v / peak, 4)})
+    # the step rate: the step replayed as one HIP graph (no launch gaps)
+    print(f"[bench] {w.name}: timing {steps} graph replays of the step", file=sys.stderr,
+          flush=True)
+    ms_step, med_step = time_graph(bench, steps, warmup)
     out = {"value": round(bench.work_step / (ms_step / 1e3) / scale_v, 2), "unit": unit,
-           "ms_per_step": round(ms_step, 4), "median_step_ms": round(_median(step_ms), 4),
+           "ms_per_step": round(ms_step, 4), "median_step_ms": round(med_step, 4),
+           "timing": "HIP graph replay of the whole step",
+           "eager": {"ms_per_step": round(eager_ms_step, 4),
+                     "median_step_ms": round(_median(eager_step_ms), 4),
+                     "value": round(bench.work_step / (eager_ms_step / 1e3) / scale_v, 2)},
            "roofline": roof}
     if getattr(bench, "merge_idx", None) is not None:
         m_ms = [step[bench.merge_idx][0].elapsed_time(step[bench.merge_idx][1]) for step in ev]
@@ -953,6 +1016,8 @@ def extra_block(name: str, steps: int, warmup: int, cpu: bool, budget_s: float) 
         block = {"metric": "step latency", "unit": "us", "higher_is_better": False,
                  "latency_us_median": round(m["median_step_ms"] * 1e3, 2),
                  "latency_us_mean": round(m["ms_per_step"] * 1e3, 2),
+                 "timing": m["timing"],
+                 "eager_latency_us_median": round(m["eager"]["median_step_ms"] * 1e3, 2),
                  "dtype": bench.dtype, "config": bench.config(),
                  "shard_partial_median_us": m["roofline"]["median_launch_us"]}
         if "merge" in m:
@@ -1021,7 +1086,7 @@ def main():
         "vs_baseline": None, "dtype": bench.dtype, "data": "synthetic", "config": bench.config(),
         "roofline": m["roofline"],
     }
-    for key in ("merge", "tokens_per_s"):
+    for key in ("timing", "eager", "merge", "tokens_per_s"):
         if key in m:
             line[key] = m[key]
     if not args.no_cpu_baseline:

@@ -1,7 +1,9 @@
 """GPU: a decode step (every shard's partial, then the merge) captured as a
 HIP graph replays to the eager step's exact bytes -- three replays, each after
 an eager step and a synchronisation, with every output poisoned before the
-replay.  (The bench times its steps this way.)"""
+replay.  (bench.py times its step rate by replaying its whole step -- slot map
+and cache write, every shard's partial, the merge -- as one graph, and checks
+the last replay against the eager step.)"""
 import pytest
 import torch
 
