@@ -162,9 +162,11 @@ class GqaDecodeBench:
         self.work_step = self.kv_bytes_step
         self.tokens_step = w.B * T  # query tokens decoded per step (one layer, all shards)
         self.per_launch_work = self.per_launch_bytes
-        self.launches_per_step = w.N + 1  # the N shard partials, then the merge
-        self.dominant = list(range(w.N))
-        self.merge_idx = w.N
+        # one event pair around the N shard calls back to back, one around the merge
+        self.launches_per_step = 2
+        self.launches_per_event = w.N
+        self.dominant = [0]
+        self.merge_idx = 1
         self.merge_bytes = (w.N + 1) * w.B * T * w.Hq * (w.D + 1) * 4
         self.kernel_name = ("cp_decode_attn_partial_gqa (attention + split combine)" if T == 1 else
                             f"cp_decode_attn_partial_gqa_mtp ({T} query tokens; attention + split "
@@ -177,9 +179,9 @@ class GqaDecodeBench:
             cp.cp_slot_map_cache_write(self.req_new, self.pos_new, sh["bt_d"], r, w.N, w.I, w.bs,
                                        self.k_new, self.v_new, sh["kc"], sh["vc"],
                                        slot_out=sh["slots"])
+        if ev is not None:
+            ev[0][0].record()
         for r, sh in enumerate(self.shards):
-            if ev is not None:
-                ev[r][0].record()
             if self.T == 1:
                 cp.cp_decode_attn_partial_gqa(self.q, sh["kc"], sh["vc"], sh["bt_d"], sh["ll_d"],
                                               w.scale, out=self.part_out[r], lse=self.part_lse[r],
@@ -189,13 +191,12 @@ class GqaDecodeBench:
                                                   sh["ll_d"], self.seq_d, w.scale, r, w.N, w.I,
                                                   out=self.part_out[r], lse=self.part_lse[r],
                                                   workspace=sh["ws"])
-            if ev is not None:
-                ev[r][1].record()
         if ev is not None:
-            ev[w.N][0].record()
+            ev[0][1].record()
+            ev[1][0].record()
         cp.cp_lse_merge(self.part_out, self.part_lse, out=self.out, lse_out=self.lse)
         if ev is not None:
-            ev[w.N][1].record()
+            ev[1][1].record()
 
     def cpu_baseline(self, budget_s=15.0, min_s=1.0):
         """The fp64 oracle on the same workload: all shard partials of whole
@@ -324,9 +325,11 @@ class MlaDecodeBench:
         eb = self.lat.element_size()
         self.per_launch_bytes = [int(sh["ll"].sum()) * w.D * eb + self.q.numel() * 2
                                  + w.B * w.Hq * (w.Dv + 1) * 4 for sh in self.shards]
-        self.launches_per_step = w.N + 1  # the N shard partials, then the merge
-        self.dominant = list(range(w.N))
-        self.merge_idx = w.N
+        # one event pair around the N shard calls back to back, one around the merge
+        self.launches_per_step = 2
+        self.launches_per_event = w.N
+        self.dominant = [0]
+        self.merge_idx = 1
         self.merge_bytes = (w.N + 1) * w.B * w.Hq * (w.Dv + 1) * 4
         self.kernel_name = "cp_decode_attn_partial_mla (attention + split combine)"
         self.dtype = "bf16"
@@ -336,19 +339,18 @@ class MlaDecodeBench:
         for r, sh in enumerate(self.shards):
             cp.cp_slot_map_cache_write(self.req_new, self.pos_new, sh["bt_d"], r, w.N, w.I, w.bs,
                                        self.lat_new, None, sh["kc"], None, slot_out=sh["slots"])
+        if ev is not None:
+            ev[0][0].record()
         for r, sh in enumerate(self.shards):
-            if ev is not None:
-                ev[r][0].record()
             cp.cp_decode_attn_partial_mla(self.q, sh["kc"], sh["bt_d"], sh["ll_d"], w.scale,
                                           Dv=w.Dv, kv_scale=self.kv_scale, out=self.part_out[r],
                                           lse=self.part_lse[r], workspace=sh["ws"])
-            if ev is not None:
-                ev[r][1].record()
         if ev is not None:
-            ev[w.N][0].record()
+            ev[0][1].record()
+            ev[1][0].record()
         cp.cp_lse_merge(self.part_out, self.part_lse, out=self.out, lse_out=self.lse)
         if ev is not None:
-            ev[w.N][1].record()
+            ev[1][1].record()
 
     def cpu_baseline(self, budget_s=15.0):
         """The fp64 oracle on the same workload: shard partials of request 0,
@@ -440,9 +442,12 @@ class PrefillBench:
         self.tokens_step = w.C  # prefill tokens per step (one layer, all PCP ranks)
         # events bracket every launch: per rank one causal-chunk call, then one
         # call per prefix shard; the prefix calls carry 80% of the work
-        self.launches_per_step = w.N * (w.N + 1)
-        self.dominant = [r * (w.N + 1) + 1 + s for r in range(w.N) for s in range(w.N)]
-        self.secondary = [r * (w.N + 1) for r in range(w.N)]
+        # per query rank: one event pair around the causal call, one around
+        # its N prefix-shard calls back to back
+        self.launches_per_step = 2 * w.N
+        self.launches_per_event = w.N
+        self.dominant = [2 * r + 1 for r in range(w.N)]
+        self.secondary = [2 * r for r in range(w.N)]
         self.per_launch_work = [self.work_prefix / (w.N * w.N)]
         self.secondary_work = self.work_causal / w.N
         kv_tok = w.Hkv * w.D * 2 * 2
@@ -457,25 +462,21 @@ class PrefillBench:
         for s, sh in enumerate(self.shards):
             cp.cp_slot_map_cache_write(self.req_c, self.pos_c, sh["bt_d"], s, w.N, w.I, w.bs,
                                        self.k, self.v, sh["kc"], sh["vc"], slot_out=sh["slots"])
-        k = 0
         for r in range(w.N):
             if ev is not None:
-                ev[k][0].record()
+                ev[2 * r][0].record()
             cp.pcp_prefill_attn_causal(self.q, w.P, r, w.N, w.scale, k=self.k, v=self.v,
                                        out=self.part_out[0], lse=self.part_lse[0])
             if ev is not None:
-                ev[k][1].record()
-            k += 1
+                ev[2 * r][1].record()
+                ev[2 * r + 1][0].record()
             for s, sh in enumerate(self.shards):
-                if ev is not None:
-                    ev[k][0].record()
                 cp.pcp_prefill_attn_causal(self.q, w.P, r, w.N, w.scale, k_cache=sh["kc"],
                                            v_cache=sh["vc"], block_table=sh["bt_row"],
                                            local_len=sh["ll"], out=self.part_out[1 + s],
                                            lse=self.part_lse[1 + s])
-                if ev is not None:
-                    ev[k][1].record()
-                k += 1
+            if ev is not None:
+                ev[2 * r + 1][1].record()
             cp.cp_lse_merge(self.part_out, self.part_lse, out=self.out[r], lse_out=self.lse[r])
 
     def cpu_baseline(self, budget_s=15.0):
@@ -556,8 +557,10 @@ class DcpPrefillBench:
         self.work_step = (causal + C * P) * w.Hq * 4 * w.D
         self.tokens_step = C  # prefill tokens per step (one layer, all ranks)
         # events bracket every shard call: per PCP rank one call per DCP shard
-        self.launches_per_step = w.N * w.N
-        self.dominant = list(range(w.N * w.N))
+        # per query rank: one event pair around its N shard calls back to back
+        self.launches_per_step = w.N
+        self.launches_per_event = w.N
+        self.dominant = list(range(w.N))
         self.per_launch_work = [self.work_step / (w.N * w.N)]
         kv_tok = w.Hkv * w.D * 2 * 2
         self.per_launch_bytes = [sum(sh["ll"] for sh in self.shards) * kv_tok / w.N / w.N
@@ -572,18 +575,16 @@ class DcpPrefillBench:
         for s, sh in enumerate(self.shards):
             cp.cp_slot_map_cache_write(self.req_c, self.pos_c, sh["bt_d"], s, w.N, w.I, w.bs,
                                        self.k_c, self.v_c, sh["kc"], sh["vc"], slot_out=sh["slots"])
-        k = 0
         for r in range(w.N):
+            if ev is not None:
+                ev[r][0].record()
             for s, sh in enumerate(self.shards):
-                if ev is not None:
-                    ev[k][0].record()
                 cp.pcp_prefill_attn_causal(self.q, w.P, r, w.N, w.scale, k_cache=sh["kc"],
                                            v_cache=sh["vc"], block_table=sh["bt_row"],
                                            local_len=sh["ll"], dcp=(s, w.N, w.I),
                                            out=self.part_out[s], lse=self.part_lse[s])
-                if ev is not None:
-                    ev[k][1].record()
-                k += 1
+            if ev is not None:
+                ev[r][1].record()
             cp.cp_lse_merge(self.part_out, self.part_lse, out=self.out[r], lse_out=self.lse[r])
 
     def cpu_baseline(self, budget_s=15.0):
@@ -880,7 +881,27 @@ def time_graph(bench, steps: int, warmup: int):
     return elapsed * 1e3 / steps, _median([a.elapsed_time(b) for a, b in sev])
 
 
-def measure(bench, steps: int, warmup: int) -> dict:
+def _spin_cycles(bench) -> int:
+    """Clock cycles of a GPU spin that outlasts the host's issue of one step
+    (three times the measured issue time, at least 2 ms)."""
+    import torch
+
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    cyc = 1 << 20
+    torch.cuda.synchronize()
+    a.record()
+    torch.cuda._sleep(cyc)
+    b.record()
+    torch.cuda.synchronize()
+    ms_per_cyc = max(a.elapsed_time(b), 1e-3) / cyc
+    t0 = time.perf_counter()
+    bench.step()
+    issue_ms = (time.perf_counter() - t0) * 1e3
+    torch.cuda.synchronize()
+    return int(min(max(3 * issue_ms, 2.0), 200.0) / ms_per_cyc)
+
+
+def measure(bench, steps: int, warmup: int, graph: bool = True) -> dict:
     """Warm up, then time exactly ``steps`` steps of ``bench`` with HIP events
     around every launch of interest and around every step (the launches'
     roofline), and exactly ``steps`` replays of the step captured as a HIP
@@ -897,16 +918,26 @@ def measure(bench, steps: int, warmup: int) -> dict:
     ev = [[mk() for _ in range(n_ev)] for _ in range(steps)]
     sev = [mk() for _ in range(steps)]
     print(f"[bench] {w.name}: timing {steps} steps", file=sys.stderr, flush=True)
+    # eager steps as the host issues them (launch gaps included)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         sev[i][0].record()
-        bench.step(ev[i])
+        bench.step()
         sev[i][1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     eager_ms_step = elapsed * 1e3 / steps
     eager_step_ms = [a.elapsed_time(b) for a, b in sev]
+    # the launches of interest, each step queued behind a GPU spin that outlasts
+    # the host's issue of the step, so the events time the kernels back to back
+    # (as a kernel trace does) and not the host's launch rate
+    spin = _spin_cycles(bench)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        torch.cuda._sleep(spin)
+        bench.step(ev[i])
+    torch.cuda.synchronize()
     per_event = getattr(bench, "launches_per_event", 1)  # launches between one event pair
     launch_ms = [step[k][0].elapsed_time(step[k][1]) / per_event for step in ev
                  for k in bench.dominant]
@@ -924,7 +955,7 @@ def measure(bench, steps: int, warmup: int) -> dict:
             "kernel": bench.kernel_name,
             "avg_launch_us": round(avg_launch_s * 1e6, 2),
             "median_launch_us": round(med_launch_s * 1e6, 2),
-            "launches_timed": len(launch_ms),
+            "launches_timed": len(launch_ms) * per_event,
             ("algorithmic_bytes_per_launch" if unit == "GB/s" else "algorithmic_flop_per_launch"):
                 int(avg_work)}
     if unit != "GB/s":
@@ -948,12 +979,15 @@ def measure(bench, steps: int, warmup: int) -> dict:
                                       "achieved": round(work / sec_s / scale_v, 2),
                                       "frac": round(work / sec_s / scale_v / peak, 4)})
     # the step rate: the step replayed as one HIP graph (no launch gaps)
-    print(f"[bench] {w.name}: timing {steps} graph replays of the step", file=sys.stderr,
-          flush=True)
-    ms_step, med_step = time_graph(bench, steps, warmup)
+    if graph:
+        print(f"[bench] {w.name}: timing {steps} graph replays of the step", file=sys.stderr,
+              flush=True)
+        ms_step, med_step = time_graph(bench, steps, warmup)
+    else:
+        ms_step, med_step = eager_ms_step, _median(eager_step_ms)
     out = {"value": round(bench.work_step / (ms_step / 1e3) / scale_v, 2), "unit": unit,
            "ms_per_step": round(ms_step, 4), "median_step_ms": round(med_step, 4),
-           "timing": "HIP graph replay of the whole step",
+           "timing": "HIP graph replay of the whole step" if graph else "eager launches",
            "eager": {"ms_per_step": round(eager_ms_step, 4),
                      "median_step_ms": round(_median(eager_step_ms), 4),
                      "value": round(bench.work_step / (eager_ms_step / 1e3) / scale_v, 2)},
@@ -1048,6 +1082,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa_decode_bf16", choices=BENCH_WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (for profiler counter passes)")
     ap.add_argument("--no-extra", action="store_true",
                     help="only the selected workload (the default run also measures "
                          + ", ".join(EXTRA_WORKLOADS) + ")")
@@ -1078,7 +1114,7 @@ def main():
     w = ci.WORKLOADS[args.workload]
     print(f"[bench] setting up {w.name}", file=sys.stderr, flush=True)
     bench = BENCHES[w.kind](w)
-    m = measure(bench, args.steps, args.warmup)
+    m = measure(bench, args.steps, args.warmup, graph=not args.no_graph)
     line = {
         "metric": METRIC, "value": m["value"], "unit": m["unit"], "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": m["ms_per_step"],
