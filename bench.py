@@ -667,18 +667,25 @@ class KvGatherBench:
         self.per_launch_work = [self.work_step]
         self.per_launch_bytes = [self.work_step]
         self.launches_per_step = 1
+        self.launches_per_event = 4
         self.dominant = [0]
         self.kernel_name = "cp_kv_gather (K and V, whole prefix)"
         self.dtype = w.kv_dtype
 
     def step(self, ev=None):
         w = self.w
-        if ev is not None:
-            ev[0][0].record()
-        self.cp.cp_kv_gather(self.kc, self.vc, self.bt, self.seq, w.N, w.I, w.bs, 0, w.P,
-                             k_out=self.k_out, v_out=self.v_out)
-        if ev is not None:
-            ev[0][1].record()
+        if ev is None:
+            self.cp.cp_kv_gather(self.kc, self.vc, self.bt, self.seq, w.N, w.I, w.bs, 0, w.P,
+                                 k_out=self.k_out, v_out=self.v_out)
+            return
+        # the timed launches: the gather repeated back to back between one
+        # event pair (an event pair around a single ~90 us launch adds its own
+        # few-us gap to it)
+        ev[0][0].record()
+        for _ in range(self.launches_per_event):
+            self.cp.cp_kv_gather(self.kc, self.vc, self.bt, self.seq, w.N, w.I, w.bs, 0, w.P,
+                                 k_out=self.k_out, v_out=self.v_out)
+        ev[0][1].record()
 
     def cpu_baseline(self, budget_s=15.0):
         """The oracle's gather (numpy over the oracle's slot map) on windows of
