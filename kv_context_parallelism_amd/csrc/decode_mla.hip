@@ -190,14 +190,6 @@ __device__ __forceinline__ int swz(int t) {
     return ((u & 1) << 2) | (u >> 1);
 }
 
-// The lane id, recomputed where it is used: keeps per-lane addresses from
-// being hoisted out of the tile loop and held in registers.
-__device__ __forceinline__ int lane_id_here() {
-    int l;
-    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-    return l;
-}
-
 // max / sum of x over lanes l and l ^ 32 (v_permlane32_swap exchanges the
 // upper half of its first operand with the lower half of its second: with x
 // in both, the two results hold x[l % 32] and x[32 + l % 32] in every lane).
@@ -315,6 +307,15 @@ mla_kernel(MlaParams p) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h0 = wave * kHW;
+    // The lane id passed through an empty asm: a fresh value at each use, so
+    // that per-lane addresses derived from it are recomputed where they are
+    // used instead of hoisted out of the tile loop into registers (no
+    // instruction, where v_mbcnt would cost two).
+    auto lane_now = [&]() -> int {
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        return l;
+    };
     const int r32 = lane & 31, h2 = lane >> 5;
     const int32_t cap = p.cap;
     const int bs = 1 << p.bs_log2;
@@ -427,7 +428,7 @@ mla_kernel(MlaParams p) {
     // ---- per-lane LDS offsets ----
     // score operand, k-step ks: row r32, chunk 2 ks + h2, i.e. group ks / 4,
     // position 2 (ks % 4) + h2 within it (swizzled)
-    const int ln = lane_id_here();  // (recomputed per segment, not carried across)
+    const int ln = lane_now();  // (recomputed per segment, not carried across)
     uint32_t kofs[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -533,7 +534,7 @@ mla_kernel(MlaParams p) {
             if (i >= ncopy) return;
             const int sl = wave + kWaves * i;
             const uint32_t dst = raw_lds + (uint32_t)((j % kRaw) * kRawTileB + sl * 1024);
-            const int l = lane_id_here();
+            const int l = lane_now();
             const int t = l & 31, pos = 2 * sl + (l >> 5);
             const int tt = min(t, ts.nval - 1);
             const int32_t row = tt < 16 ? ts.r0 + tt : ts.r1 - 16 + tt;
@@ -541,7 +542,7 @@ mla_kernel(MlaParams p) {
         } else {
             const uint32_t dst = kv_lds + (uint32_t)((j % kStagesBf) * kTileB + i * kGroupB +
                                                      8 * wave * 128);
-            const int t = 8 * wave + (lane_id_here() >> 3);
+            const int t = 8 * wave + (lane_now() >> 3);
             const int tt = min(t, ts.nval - 1);
             const int32_t row = tt < 16 ? ts.r0 + tt : ts.r1 - 16 + tt;
             dma16(p.kv + (int64_t)row * kRowB + ccol + 128 * i, __builtin_amdgcn_readfirstlane(dst));
@@ -567,12 +568,12 @@ mla_kernel(MlaParams p) {
                 if (i >= ncopy) break;
                 const int sl = wave + kWaves * i;
                 xs[i] = *(__attribute__((address_space(3))) const u32x4_t *)(raw + sl * 1024 +
-                                                                               16 * lane_id_here());
+                                                                               16 * lane_now());
             }
 #pragma unroll
             for (int i = 0; i < kNc; ++i) {
                 if (i >= ncopy) break;
-                const int l = lane_id_here();
+                const int l = lane_now();
                 const int t = l & 31, pos = 2 * (wave + kWaves * i) + (l >> 5);
                 const u32x4_t x = xs[i];
                 u32x4_t lo2, hi2;
@@ -690,13 +691,20 @@ mla_kernel(MlaParams p) {
     // operands) are read by vp_begin, which the caller issues early.
     struct VpOps {
         VBase tv;
+        uint32_t pp;  // this lane's probabilities in parity buffer pb (entry [0][0])
         u32x4_t pa[kHb][2];
         u32x4_t vq[3];
     };
+    // probabilities of head block hb, 16-token step kk: an immediate offset from op.pp
+    auto read_p = [&](const VpOps &op, int hb, int kk) -> u32x4_t {
+        return *(__attribute__((address_space(3))) const u32x4_t *)(
+            (lds_u8 *)(uintptr_t)op.pp + (hb * 2 + kk) * 64 * 16);
+    };
     auto vp_begin = [&](uint32_t t, int pb, VpOps &op) {
         op.tv = v_base(t);
+        op.pp = opaque((uint32_t)(uintptr_t)(lds_u8 *)(&s_p[pb][0][0][0]) + 16u * (uint32_t)lane);
 #pragma unroll
-        for (int hb = 0; hb < kHb; ++hb) op.pa[hb][0] = s_p[pb][hb][0][lane_id_here()];
+        for (int hb = 0; hb < kHb; ++hb) op.pa[hb][0] = read_p(op, hb, 0);
         op.vq[0] = read_v(op.tv, 0, 0);
         op.vq[1] = read_v(op.tv, 0, 1);
     };
@@ -711,7 +719,7 @@ mla_kernel(MlaParams p) {
             if (j + 2 < 2 * kCbW) vq[(j + 2) % 3] = read_v(tv, (j + 2) >> 2, (j + 2) & 3);
             if (j == 0)
 #pragma unroll
-                for (int hb = 0; hb < kHb; ++hb) pa[hb][1] = s_p[pb][hb][1][lane_id_here()];
+                for (int hb = 0; hb < kHb; ++hb) pa[hb][1] = read_p(op, hb, 1);
 #pragma unroll
             for (int hb = 0; hb < kHb; ++hb) {
                 mfma32_a(o[4 * hb + (j & 3)], pa[hb][j >> 2], vb);
@@ -749,7 +757,7 @@ mla_kernel(MlaParams p) {
             __builtin_amdgcn_sched_barrier(0);
             mfma_drain();  // the value-product MFMAs issued last write the AGPRs read below
             __builtin_amdgcn_sched_barrier(0);
-            const int hh = 4 * (lane_id_here() >> 5);
+            const int hh = 4 * (lane_now() >> 5);
 #pragma unroll
             for (int hb = 0; hb < kHb; ++hb) {
                 const int32_t fl = hb == 0 ? f0 : hb == 1 ? f1 : hb == 2 ? f2 : f3;
@@ -813,7 +821,7 @@ mla_kernel(MlaParams p) {
         // rows past its end repeat its last row)
         gbyte *csrc = nullptr;
         if (!kFp8 && copy_now) {
-            const int t = 8 * wave + (lane_id_here() >> 3);
+            const int t = 8 * wave + (lane_now() >> 3);
             const int tt = min(t, nsrc.nval - 1);
             const int32_t row = tt < 16 ? nsrc.r0 + tt : nsrc.r1 - 16 + tt;
             uint64_t a = (uint64_t)(uintptr_t)(p.kv + (int64_t)row * kRowB + ccol);
@@ -874,7 +882,7 @@ mla_kernel(MlaParams p) {
         float mt = 0.f;
         auto soft_mask = [&]() {
             if (nval < kT) {  // token acc_row(e, h2) = acc_row(e, 0) + 4 h2 is real iff < nval
-                const int lim = nval - 4 * (lane_id_here() >> 5);
+                const int lim = nval - 4 * (lane_now() >> 5);
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
                     if (acc_row(e, 0) >= lim) sc[e] = -INFINITY;
@@ -919,12 +927,12 @@ mla_kernel(MlaParams p) {
             ps += pe0 + pe1;
         };
         auto publish_p = [&]() {
-            const int ln2 = lane_id_here();
+            const int ln2 = lane_now();
             s_p[it & 1][wave][0][ln2] = Pn[0];
             s_p[it & 1][wave][1][ln2] = Pn[1];
         };
         auto publish_alpha = [&]() {
-            const int ln2 = lane_id_here();
+            const int ln2 = lane_now();
             if (ln2 < 32) s_alpha[it & 1][wave][ln2] = alpha;
             if (ln2 == 0) s_aflag[it & 1][wave] = resc ? 1 : 0;
         };
