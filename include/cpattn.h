@@ -189,10 +189,14 @@ size_t cp_noalloc_scratch_bytes(void);
  * LSE -inf.
  *   base.q   [B][q_len][Hq][D], base.out [B][q_len][Hq][D] fp32,
  *   base.lse [B][q_len][Hq] fp32; other base fields as cp_gqa_args.
- * Supported: 256-byte K/V rows (bf16 D 128 or fp32 D 64) with
- * q_len * Hq/Hkv in {1, 2, 4, 8}.  seq_len[b] < q_len gives NaN rows.
- * Workspace: cp_workspace_bytes(CP_OP_DECODE_GQA_MTP, &args); need not be
- * initialised.
+ * Supported: 256-byte K/V rows (bf16 D 128 or fp32 D 64), Hq/Hkv in
+ * {1, 2, 4, 8}, any q_len >= 1.  The tokens are processed in launches of at
+ * most 8 / (Hq/Hkv) tokens (8 query rows per KV head), one after the other on
+ * the stream; each launch reads the shard's K/V once, so q_len * Hq/Hkv above
+ * 8 costs ceil(q_len * Hq/Hkv / 8) or more passes over the shard.
+ * seq_len[b] < q_len gives NaN rows.
+ * Workspace: cp_workspace_bytes(CP_OP_DECODE_GQA_MTP, &args) (one launch's
+ * partials, reused by the next); need not be initialised.
  * Errors: as cp_decode_attn_partial_gqa, plus CP_E_INVALID for q_len < 1, a
  * rank outside [0, dcp_size), interleave < 1, NULL seq_len; CP_E_UNSUPPORTED
  * for other shapes. */

@@ -415,11 +415,16 @@ static GqaPlan plan_rows(const cp_gqa_args &a, int T, bool mtp) {
     return pl;
 }
 
+// Multi-token decode: the request's q_len tokens in launches of Tg tokens
+// (Tg Hq/Hkv rows of at most 8 per KV head, the row kernel's widest form),
+// one after the other on the stream; the workspace holds one launch's
+// partials and is reused.
 GqaPlan plan_gqa_mtp(const cp_gqa_mtp_args &m) {
     const cp_gqa_args &a = m.base;
-    if (a.Hkv < 1 || a.Hq % a.Hkv != 0 || m.q_len < 1 || !gqa_rows_supported(a, m.q_len))
-        return GqaPlan{};
-    return plan_rows(a, m.q_len, true);
+    if (a.Hkv < 1 || a.Hq % a.Hkv != 0 || m.q_len < 1) return GqaPlan{};
+    const int Tg = gqa_mtp_group_tokens(a, m.q_len);
+    if (Tg < 1 || !gqa_rows_supported(a, Tg)) return GqaPlan{};
+    return plan_rows(a, Tg, true);
 }
 
 GqaPlan plan_gqa(const cp_gqa_args &a) {
@@ -475,11 +480,12 @@ cp_status validate_gqa(const cp_gqa_args *a) {
 
 namespace {
 
-// The row-layout kernel and its split combine: T x Hq/Hkv rows per KV head,
-// merged into out [B][T][Hq][D] and lse [B][T][Hq].
+// The row-layout kernel and its split combine: Tg x Hq/Hkv rows per KV head
+// (tokens t0 .. t0 + Tg - 1 of T), merged into out [B][T][Hq][D] and
+// lse [B][T][Hq].
 cp_status run_rows(const cp_gqa_args *a, int bs_log2, void *ws, const GqaPlan &pl,
                    const GqaMtp &mtp, hipStream_t stream) {
-    const int T = mtp.T;
+    const int T = mtp.Tg > 0 ? mtp.Tg : mtp.T;
     const int G = a->Hq / a->Hkv * T;
     const size_t slots = (size_t)pl.waves + (size_t)a->B * a->Hkv;
     float *ws_o = static_cast<float *>(ws);
@@ -506,6 +512,8 @@ cp_status run_rows(const cp_gqa_args *a, int bs_log2, void *ws, const GqaPlan &p
     m.remap_T = T;
     m.remap_G = a->Hq / a->Hkv;
     m.remap_Hkv = a->Hkv;
+    m.remap_Tfull = mtp.T;
+    m.remap_t0 = mtp.t0;
     return launch_merge(m, stream);
 }
 
@@ -524,11 +532,12 @@ extern "C" cp_status cp_decode_attn_partial_gqa_mtp(const cp_gqa_mtp_args *m, vo
         return fail(CP_E_INVALID, "gqa mtp decode: q_len=%d dcp rank %d of %d, interleave %d",
                     m->q_len, m->dcp_rank, m->dcp_size, m->interleave);
     if (!m->seq_len) return fail(CP_E_INVALID, "gqa mtp decode: NULL seq_len");
-    if (!gqa_rows_supported(*a, m->q_len))
+    const int tg_max = gqa_mtp_group_tokens(*a, m->q_len);
+    if (tg_max < 1 || !gqa_rows_supported(*a, tg_max))
         return fail(CP_E_UNSUPPORTED,
-                    "gqa mtp decode: q_len x Hq/Hkv = %d (the row kernel takes 1, 2, 4 or 8 rows "
-                    "per KV head of 256-byte K/V rows)",
-                    m->q_len * (a->Hq / a->Hkv));
+                    "gqa mtp decode: Hq/Hkv = %d, D = %d (the row kernel takes groups of 1, 2, 4 "
+                    "or 8 heads with 256-byte K/V rows)",
+                    a->Hq / a->Hkv, a->D);
     const GqaPlan pl = plan_gqa_mtp(*m);
     if (!ws || ws_bytes < pl.ws_bytes)
         return fail(CP_E_WORKSPACE, "gqa mtp decode: workspace of %zu bytes needed, %zu given",
@@ -539,7 +548,17 @@ extern "C" cp_status cp_decode_attn_partial_gqa_mtp(const cp_gqa_mtp_args *m, vo
     mtp.dcp_rank = m->dcp_rank;
     mtp.dcp_size = m->dcp_size;
     mtp.dcp_I = m->interleave;
-    return run_rows(a, log2_exact(a->bs), ws, pl, mtp, stream);
+    // launches of tg_max tokens, then the largest power of two that the rest allows
+    for (int t0 = 0; t0 < m->q_len;) {
+        int tg = m->q_len - t0 < tg_max ? m->q_len - t0 : tg_max;
+        while (tg & (tg - 1)) tg &= tg - 1;
+        mtp.t0 = t0;
+        mtp.Tg = tg;
+        const cp_status st2 = run_rows(a, log2_exact(a->bs), ws, pl, mtp, stream);
+        if (st2 != CP_OK) return st2;
+        t0 += tg;
+    }
+    return CP_OK;
 }
 
 extern "C" cp_status cp_decode_attn_partial_gqa(const cp_gqa_args *a, void *ws, size_t ws_bytes,

@@ -63,12 +63,13 @@ struct RowParams {
     float *ws_o;      // [slots][G][D]
     float *ws_l;      // [slots][G]
     int32_t *seg;     // [B*Hkv][2]: first slot, count
-    // Multi-token queries: the kernel's G = T x Greal rows per KV head are
-    // query token t (the request's position seq_len - T + t) of head
-    // g Greal + h, row t Greal + h.  Token t sees the shard's keys at
+    // Multi-token queries: the kernel's G = Tg x Greal rows per KV head are
+    // query token t0 + t (the request's position seq_len - T + t0 + t) of
+    // head g Greal + h, row t Greal + h, for the launch's Tg tokens t0 ..
+    // t0 + Tg - 1 of the request's T.  A token sees the shard's keys at
     // positions <= its own (seq_len == nullptr: T = 1, no limit).
     const int32_t *seq_len;
-    int32_t T, Greal;
+    int32_t T, t0, Greal;
     int32_t dcp_rank, dcp_size, dcp_I;
 };
 
@@ -269,10 +270,11 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
         cint32 *bt_row = p.bt + (int64_t)b * p.bt_stride;
         // Key limits: row hh (query token hh / Greal) sees local keys below
         // lim[k2] of this piece; min_lim is the first token's, the smallest.
-        int32_t qpos0 = 0;  // position of query token 0
+        int32_t qpos0 = 0;  // position of the launch's query token 0 (token t0 of the request)
         if constexpr (kMtp) {
-            qpos0 = p.seq_len[b] - p.T;
-            bad |= qpos0 < 0;
+            const int32_t first = p.seq_len[b] - p.T;  // position of the request's first query token
+            bad |= first < 0;
+            qpos0 = first + p.t0;
         }
         auto causal_lim = [&](int t) -> int32_t {
             if constexpr (!kMtp) return s1;
@@ -338,7 +340,7 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
             const int t = hh / p.Greal, h = hh - t * p.Greal;
-            qraw[hh] = load16(p.q + (((int64_t)b * p.T + t) * p.Hq + g * p.Greal + h) * 256 + c * 16);
+            qraw[hh] = load16(p.q + (((int64_t)b * p.T + p.t0 + t) * p.Hq + g * p.Greal + h) * 256 + c * 16);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         float qf[kBf16 ? 1 : G][4];
@@ -603,6 +605,12 @@ bool gqa_rows_supported(const cp_gqa_args &a, int T) {
     return row256 && (G == 1 || G == 2 || G == 4 || G == 8) && a.B <= kMaxB;
 }
 
+int gqa_mtp_group_tokens(const cp_gqa_args &a, int T) {
+    const int Greal = a.Hkv > 0 ? a.Hq / a.Hkv : 0;
+    if (Greal < 1 || Greal > 8 || (Greal & (Greal - 1)) || T < 1) return 0;
+    return T < 8 / Greal ? T : 8 / Greal;
+}
+
 int gqa_rows_waves(const cp_gqa_args &a, int T, bool mtp) {
     (void)a;
     (void)T;
@@ -631,11 +639,12 @@ cp_status gqa_rows_launch(const cp_gqa_args &a, int bs_log2, float *ws_o, float 
     p.seg = seg;
     p.seq_len = mtp.seq_len;
     p.T = mtp.T;
+    p.t0 = mtp.t0;
     p.Greal = a.Hq / a.Hkv;
     p.dcp_rank = mtp.dcp_rank;
     p.dcp_size = mtp.dcp_size;
     p.dcp_I = mtp.dcp_I;
-    const int G = a.Hq / a.Hkv * mtp.T;  // rows per KV head
+    const int G = a.Hq / a.Hkv * (mtp.Tg > 0 ? mtp.Tg : mtp.T);  // rows per KV head
     if (a.dt == CP_BF16) {
         switch (G) {
         case 1: return launch_rows<2, 1>(p, stream);

@@ -74,20 +74,24 @@ struct MergeDesc {
     void *out;
     cp_dtype out_dt;
     float *lse_out;
-    // Output row of merge row r when remap_T > 1 (multi-token decode: merge
-    // rows are (request, KV head, token, head in group); outputs are
-    // [request][token][Hq]): see merge_out_row.
+    // Output row of merge row r in multi-token decode: merge rows are
+    // (request, KV head, token of the group, head in group), remap_T tokens
+    // per group; outputs are [request][remap_Tfull][Hq] with the group's
+    // tokens at remap_t0 .. (remap_Tfull 0: the group is every token).  See
+    // merge_out_row.
     int32_t remap_T = 1, remap_G = 1, remap_Hkv = 1;
+    int32_t remap_Tfull = 0, remap_t0 = 0;
 };
 cp_status launch_merge(const MergeDesc &m, hipStream_t stream);
 
 __host__ __device__ inline int64_t merge_out_row(const MergeDesc &m, int64_t r) {
-    if (m.remap_T <= 1) return r;
+    const int64_t Tf = m.remap_Tfull > 0 ? m.remap_Tfull : m.remap_T;
+    if (Tf <= 1) return r;
     const int64_t per = (int64_t)m.remap_T * m.remap_G;  // rows per (request, KV head)
     const int64_t seg = r / per, sub = r - seg * per;
     const int64_t b = seg / m.remap_Hkv, g = seg - b * m.remap_Hkv;
     const int64_t t = sub / m.remap_G, h = sub - t * m.remap_G;
-    return (b * m.remap_T + t) * ((int64_t)m.remap_Hkv * m.remap_G) + g * m.remap_G + h;
+    return (b * Tf + m.remap_t0 + t) * ((int64_t)m.remap_Hkv * m.remap_G) + g * m.remap_G + h;
 }
 
 // Compute units of the current device (cached per device).
@@ -100,8 +104,12 @@ struct GqaMtp {
     int32_t T = 1;
     const int32_t *seq_len = nullptr;
     int32_t dcp_rank = 0, dcp_size = 1, dcp_I = 1;
+    // the tokens of one launch: t0 .. t0 + Tg - 1 of the T (Tg 0: all T)
+    int32_t t0 = 0, Tg = 0;
 };
 bool gqa_rows_supported(const cp_gqa_args &a, int T = 1);
+// tokens per launch of the multi-token entry: G = Tg Hq/Hkv rows must be 1, 2, 4 or 8
+int gqa_mtp_group_tokens(const cp_gqa_args &a, int T);
 int gqa_rows_waves(const cp_gqa_args &a, int T = 1, bool mtp = false);
 cp_status gqa_rows_launch(const cp_gqa_args &a, int bs_log2, float *ws_o, float *ws_l,
                           int32_t *seg, int32_t W, const GqaMtp &mtp, hipStream_t stream);

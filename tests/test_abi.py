@@ -249,13 +249,24 @@ def test_gqa_mtp_validation():
                           dt=_lib.CP_BF16, out=16, lse=16)
     good = dict(q_len=2, dcp_rank=1, dcp_size=4, interleave=16, seq_len=16)
     for field, bad, code in [("q_len", 0, 1), ("dcp_rank", 4, 1), ("dcp_rank", -1, 1),
-                             ("dcp_size", 0, 1), ("interleave", 0, 1), ("seq_len", None, 1),
-                             ("q_len", 3, 2), ("q_len", 4, 2)]:
+                             ("dcp_size", 0, 1), ("interleave", 0, 1), ("seq_len", None, 1)]:
         kw = dict(good)
         kw[field] = bad
         m = _lib.CpGqaMtpArgs(base=base, **kw)
         assert lib.cp_decode_attn_partial_gqa_mtp(ctypes.byref(m), None, 0, None) == code, (field, bad)
-    # q_len 2 x group 4 = 8 rows per KV head: supported, so only the workspace is missing
-    m = _lib.CpGqaMtpArgs(base=base, **good)
-    assert lib.cp_decode_attn_partial_gqa_mtp(ctypes.byref(m), None, 0, None) == 3
-    assert lib.cp_workspace_bytes(_lib.CP_OP_DECODE_GQA_MTP, ctypes.byref(m)) > 0
+    # group 4: q_len 2 is 8 rows per KV head (one launch); q_len 3, 4 and 7 are
+    # taken in launches of at most 2 tokens.  All supported, so only the
+    # workspace is missing -- and it is sized for one launch of 2 tokens.
+    sizes = {}
+    for q_len in (1, 2, 3, 4, 7):
+        m = _lib.CpGqaMtpArgs(base=base, **dict(good, q_len=q_len))
+        assert lib.cp_decode_attn_partial_gqa_mtp(ctypes.byref(m), None, 0, None) == 3, q_len
+        sizes[q_len] = lib.cp_workspace_bytes(_lib.CP_OP_DECODE_GQA_MTP, ctypes.byref(m))
+    assert 0 < sizes[1] < sizes[2] == sizes[3] == sizes[4] == sizes[7]
+    # groups the row kernel does not take: 16 heads per KV head, or D 64 in bf16
+    for over in (dict(Hq=32, Hkv=2), dict(D=64)):
+        b2 = _lib.CpGqaArgs(**{f: getattr(base, f) for f, _ in base._fields_})
+        for f, v in over.items():
+            setattr(b2, f, v)
+        m = _lib.CpGqaMtpArgs(base=b2, **good)
+        assert lib.cp_decode_attn_partial_gqa_mtp(ctypes.byref(m), None, 0, None) == 2, over

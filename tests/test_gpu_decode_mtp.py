@@ -70,12 +70,21 @@ def _check(case, q, T, o, l, reqs):
 # f32 head dim 64 (group 4, 2 tokens = 8 rows per KV head); bf16 head dim 128
 # with group 4 x 2 tokens, group 1 x 8 tokens, group 2 x 4 tokens; requests as
 # short as the token count (shards without a visible key for early tokens),
-# ragged lengths around tile and interleave boundaries
+# ragged lengths around tile and interleave boundaries.  Past 8 rows per KV
+# head the tokens go in several launches: group 4 x 3 tokens (2 + 1), group
+# 4 x 4 (2 + 2), group 8 x 2 (1 + 1), group 2 x 5 (4 + 1), group 1 x 11
+# (8 + 2 + 1), f32 group 4 x 3.
 @pytest.mark.parametrize("name,T,Hq,Hkv,seq", [
     ("gqa_tiny_f32", 2, 8, 2, [1000, 33, 2, 517]),
     ("gqa_decode_bf16", 2, 32, 8, [4097, 2, 130, 9000]),
     ("gqa_decode_bf16", 8, 8, 8, [8, 300, 2049]),
     ("gqa_decode_bf16", 4, 16, 8, [5000, 4, 777]),
+    ("gqa_decode_bf16", 3, 32, 8, [3, 4097, 531]),
+    ("gqa_decode_bf16", 4, 32, 8, [100, 200, 6000]),
+    ("gqa_decode_bf16", 2, 64, 8, [2, 2500, 129]),
+    ("gqa_decode_bf16", 5, 16, 8, [5, 1030, 3333]),
+    ("gqa_decode_bf16", 11, 8, 8, [11, 700, 4100]),
+    ("gqa_tiny_f32", 3, 8, 2, [1000, 3, 260]),
 ])
 def test_mtp_against_oracle(name, T, Hq, Hkv, seq):
     base = ci.WORKLOADS[name]
@@ -111,14 +120,19 @@ def test_mtp_full_size_sampled():
 
 
 def test_mtp_rejects_unsupported_and_invalid():
+    # a group of 16 query heads per KV head is not a row-kernel shape
+    w16 = ci.scaled(ci.WORKLOADS["gqa_decode_bf16"], B=2, Hq=16, Hkv=1, seed=6502)
+    case16, q16 = _mtp_case(w16, 2, [100, 200], 6503)
+    sh = case16.shards[0]
+    with pytest.raises(cp.CpError) as e:
+        cp.cp_decode_attn_partial_gqa_mtp(q16, sh["kc"], sh["vc"], sh["bt_dev"], sh["ll_dev"],
+                                          torch.from_numpy(case16.seq).to(DEV), w16.scale, 0,
+                                          w16.N, w16.I)
+    assert e.value.status == cp.CP_E_UNSUPPORTED
     w = ci.scaled(ci.WORKLOADS["gqa_decode_bf16"], B=2, seed=6500)
-    case, q = _mtp_case(w, 4, [100, 200], 6501)   # 4 tokens x group 4 = 16 rows
+    case, q = _mtp_case(w, 4, [100, 200], 6501)
     sh = case.shards[0]
     seq_dev = torch.from_numpy(case.seq).to(DEV)
-    with pytest.raises(cp.CpError) as e:
-        cp.cp_decode_attn_partial_gqa_mtp(q, sh["kc"], sh["vc"], sh["bt_dev"], sh["ll_dev"],
-                                          seq_dev, w.scale, 0, w.N, w.I)
-    assert e.value.status == cp.CP_E_UNSUPPORTED
     with pytest.raises(cp.CpError):
         cp.cp_decode_attn_partial_gqa_mtp(q[:, :2].contiguous(), sh["kc"], sh["vc"],
                                           sh["bt_dev"], sh["ll_dev"], seq_dev, w.scale, w.N,
@@ -128,5 +142,12 @@ def test_mtp_rejects_unsupported_and_invalid():
     o, l = cp.cp_decode_attn_partial_gqa_mtp(q[:, :2].contiguous(), sh["kc"], sh["vc"],
                                              sh["bt_dev"], sh["ll_dev"], short, w.scale, 0, w.N,
                                              w.I)
+    torch.cuda.synchronize()
+    assert torch.isnan(l[0]).all() and not torch.isnan(l[1]).any()
+    # the same over two launches of two tokens (4 tokens x group 4): every
+    # token of the short request is NaN, whichever launch takes it
+    short = torch.tensor([3, 200], dtype=torch.int32, device=DEV)
+    o, l = cp.cp_decode_attn_partial_gqa_mtp(q, sh["kc"], sh["vc"], sh["bt_dev"], sh["ll_dev"],
+                                             short, w.scale, 0, w.N, w.I)
     torch.cuda.synchronize()
     assert torch.isnan(l[0]).all() and not torch.isnan(l[1]).any()
