@@ -60,6 +60,7 @@ constexpr int kTileB = kBN * kRowB;      // one K or V tile in LDS (16 KB)
 constexpr int kSlots = 2 * kTileB / 1024;  // 64-lane copies per K+V tile pair (32)
 constexpr int kMaxWaves = 8;
 constexpr float kLazy = 8.f;
+constexpr float kLazyW = 256.f;  // 2^kLazy
 // A wave reads tile it's K and tile it - 1's V in iteration it, while the
 // copies of tiles it + 1 .. it + kPf are in flight: a ring of kPf + 2 K/V tile
 // pairs (32 KB each).
@@ -342,49 +343,61 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
                 for (int e = 0; e < 16; ++e)
                     if (32 * kb + acc_row(e, 0) >= lim) sc[kb][e] = -INFINITY;
         }
-        float m = sc[0][0];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = (kb == 0 ? 1 : 0); e < 16; ++e) m = fmaxf(m, sc[kb][e]);
-        m = fmaxf(m, __shfl_xor(m, 32, 64));
-        const float mt = m * p.qk_scale;  // the scale is positive: max commutes with it
-        const bool need = mt > m_ref + kLazy;
-        if (__any(need)) {
-            // raise the reference maximum of the rows that need it and rescale
-            // their partial sums and output rows acc_row(e, hf)
-            const float mn = need ? mt : m_ref;
-            const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - mn);
-            m_ref = mn;
-            l_run *= alpha;
-            float ar[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) ar[e] = __shfl(alpha, acc_row(e, hf), 64);
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) o[db][e] *= ar[e];
-        }
-        // p = 2^(s * scale - m_ref); a row with no visible key yet keeps the
-        // reference at -inf and shifts by 0.  (The denominator is summed in
-        // fp32: the LSE needs more than the bf16 precision of the weights.)
-        const float ms = m_ref == -INFINITY ? 0.f : m_ref;
-        float ps = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                sc[kb][e] = fast_exp2(fmaf(sc[kb][e], p.qk_scale, -ms));
-                ps += sc[kb][e];
-            }
-        l_run += ps;
         // P as the A operand of 16-key step kk: elements 8 (kk % 2) .. +7 of
-        // key block kk / 2, in order
+        // key block kk / 2, in order.  p = 2^(s * scale - m_ref); a row with no
+        // visible key yet keeps the reference at -inf and shifts by 0.  (The
+        // denominator is summed in fp32: the LSE needs more than the bf16
+        // precision of the weights.)
+        float ps = 0.f;
+        auto weights = [&]() {
+            const float ms = m_ref == -INFINITY ? 0.f : m_ref;
+            ps = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+            for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                pa[kk][i] = pack_bf16x2(sc[kk >> 1][8 * (kk & 1) + 2 * i], sc[kk >> 1][8 * (kk & 1) + 2 * i + 1]);
+                for (int i = 0; i < 4; ++i) {
+                    const float x0 = fast_exp2(fmaf(sc[kk >> 1][8 * (kk & 1) + 2 * i], p.qk_scale, -ms));
+                    const float x1 = fast_exp2(fmaf(sc[kk >> 1][8 * (kk & 1) + 2 * i + 1], p.qk_scale, -ms));
+                    ps += x0;
+                    ps += x1;
+                    pa[kk][i] = pack_bf16x2(x0, x1);
+                }
+        };
+        // The weights are taken against the current reference first, without
+        // the tile's maximum: a lane whose weights sum to at most 2^kLazy has
+        // none above 2^kLazy, which is all the lazy reference asks for.  Where
+        // a weight may be larger (or overflowed, or is NaN), or a row with a
+        // visible key in the tile has no reference yet, the tile's maximum is
+        // taken, the reference raised where it must be, and the weights taken
+        // again (a uniform branch; rare after a row's first tile).
+        weights();
+        if (__any(!(ps <= kLazyW) || (m_ref == -INFINITY && klim_r > j0))) {
+            float m = sc[0][0];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = (kb == 0 ? 1 : 0); e < 16; ++e) m = fmaxf(m, sc[kb][e]);
+            m = fmaxf(m, __shfl_xor(m, 32, 64));
+            const float mt = m * p.qk_scale;  // the scale is positive: max commutes with it
+            const bool need = mt > m_ref + kLazy;
+            if (__any(need)) {
+                // raise the reference maximum of the rows that need it and rescale
+                // their partial sums and output rows acc_row(e, hf)
+                const float mn = need ? mt : m_ref;
+                const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - mn);
+                m_ref = mn;
+                l_run *= alpha;
+                float ar[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) ar[e] = __shfl(alpha, acc_row(e, hf), 64);
+#pragma unroll
+                for (int db = 0; db < 4; ++db)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) o[db][e] *= ar[e];
+            }
+            weights();
+        }
+        l_run += ps;
     };
 
     // Per-lane LDS byte offsets inside a tile, computed once.  Score operand of
