@@ -92,6 +92,7 @@ constexpr int kMaxB = 4096;
 constexpr int kChunkB = 64;              // requests per prefix-sum chunk
 constexpr int kMaxChunks = kMaxB / kChunkB;
 constexpr float kLazy = 8.f;             // rescale only past 2^8
+constexpr float kLazyW = 256.f;          // 2^kLazy
 constexpr int kTabTiles = 1024;          // tile rows held in LDS (longer segments load them)
 // bf16: ring of 3 tiles, tile it + 1 copied while tiles it and it - 1 are
 // read; wave w copies rows 8 w .. 8 w + 7 of every tile (nine 64-lane copies)
@@ -926,6 +927,27 @@ mla_kernel(MlaParams p) {
             Pn[e2 >> 2][e2 & 3] = pack_bf16x2(pe0, pe1);
             ps += pe0 + pe1;
         };
+        // Past the first tile the weights are taken against the current
+        // reference without the tile's maximum: a lane whose weights sum to at
+        // most 2^kLazy has none above 2^kLazy, which is all the lazy reference
+        // asks for.  Where a weight may be larger (or overflowed, or is NaN)
+        // the maximum is taken, the reference raised where it must be, and the
+        // weights taken again (a uniform branch; rare once the reference has
+        // settled).
+        auto soft_check = [&]() {
+            if (__any(!(ps <= kLazyW))) {
+                soft_max_lo();
+                soft_max_hi();
+                soft_halves();
+                soft_ref();
+                ps = 0.f;
+#pragma unroll
+                for (int e2 = 0; e2 < 8; ++e2) {
+                    soft_exp(e2);
+                    soft_pack(e2);
+                }
+            }
+        };
         auto publish_p = [&]() {
             const int ln2 = lane_now();
             s_p[it & 1][wave][0][ln2] = Pn[0];
@@ -940,20 +962,15 @@ mla_kernel(MlaParams p) {
             rescale_pending(flags, (it - 1) & 1);
             // the softmax steps after MFMAs 1 .. 30 of the value product
             value_product(vop, (it - 1) & 1, [&](int i) {
-                if (i == 1) {
-                    soft_mask();
-                    soft_max_lo();
-                }
-                if (i == 2) soft_max_hi();
-                if (i == 3) soft_halves();
-                if (i == 5) soft_ref();
+                if (i == 1) soft_mask();
                 // pair k: exponentials after MFMA kSlot[2 k], packing after kSlot[2 k + 1]
-                constexpr int kSlot[16] = {6, 7, 9, 10, 12, 13, 15, 16, 18, 19, 21, 22, 24, 25, 27, 28};
+                constexpr int kSlot[16] = {2, 3, 5, 6, 8, 9, 11, 12, 14, 15, 17, 18, 20, 21, 23, 24};
 #pragma unroll
                 for (int k2 = 0; k2 < 8; ++k2) {
                     if (i == kSlot[2 * k2]) soft_exp(k2);
                     if (i == kSlot[2 * k2 + 1]) soft_pack(k2);
                 }
+                if (i == 26) soft_check();
                 if (i == 29) publish_p();
                 if (i == 30) publish_alpha();
             });
