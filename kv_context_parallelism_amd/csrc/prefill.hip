@@ -139,6 +139,18 @@ __device__ __forceinline__ void dma16(gbyte *src, uint32_t lds) {
 }
 #pragma clang diagnostic pop
 
+// The same copy from base + off, with base wave-uniform (an SGPR pair) and off
+// a per-lane 32-bit byte offset: the address is formed by the instruction.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_s(gbyte *base, uint32_t off, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(lds), "v"(off), "s"(base)
+                 : "m0");
+}
+#pragma clang diagnostic pop
+
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void vm_wait() {
@@ -454,7 +466,7 @@ __global__ void __launch_bounds__(64 * kMaxWaves) prefill_kernel(PrefillParams p
         auto side = [&](int step) {
             if ((step & 7) != 7 || !spread) return;
             const int k = step >> 3;
-            dma16(csrc[k] + off8, dstn + (uint32_t)(k * 8 * 1024));
+            dma16_s(csrc[k], off8, dstn + (uint32_t)(k * 8 * 1024));
         };
         if (pre && !spread) {
             const TileSrc ts = stage_rows(jn);
