@@ -186,7 +186,26 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
         if (L < 0 || (int64_t)L > cap) return 1;
         return (L + kTile - 1) / kTile;
     };
-    {
+    // Below 64 requests every wave scans the chunk counts by itself (lane l
+    // holds request l's exclusive prefix, lane B the total): no LDS, no
+    // barrier, and a chunk's request is one ballot.  More requests take the
+    // workgroup-wide scan into LDS and a binary search.
+    const bool wave_pref = p.B < 64;
+    int32_t prefv = 0;
+    if (wave_pref) {
+        const int32_t cnt = lane < p.B ? chunks_of(p.len[lane]) : 0;
+        int32_t incl = cnt;
+#pragma unroll
+        for (int x = 1; x < 64; x <<= 1) {
+            const int32_t o = __shfl_up(incl, x, 64);
+            if (lane >= x) incl += o;
+        }
+        prefv = incl - cnt;
+        if (blockIdx.x == 0) {  // workgroup 0 publishes the segment table from LDS below
+            if (tid <= p.B) s_pref[tid] = prefv;
+            __syncthreads();
+        }
+    } else {
         const int per = (p.B + 64 * kWaves - 1) / (64 * kWaves);
         const int b0 = tid * per;
         int32_t run = 0;
@@ -215,7 +234,9 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
     // scheduled wave owns at least one chunk and the waves covering one
     // (request, head) are consecutive -- which makes its partial slots consecutive.
     // values read back from LDS are the same in every lane: keep them scalar
-    auto pref = [&](int i) -> int32_t { return __builtin_amdgcn_readfirstlane(s_pref[i]); };
+    auto pref = [&](int i) -> int32_t {
+        return wave_pref ? __builtin_amdgcn_readlane(prefv, i) : __builtin_amdgcn_readfirstlane(s_pref[i]);
+    };
     const int64_t R_tot = (int64_t)p.Hkv * pref(p.B);
     const int64_t W = R_tot < p.W ? R_tot : p.W;
 
@@ -245,10 +266,15 @@ __global__ void __launch_bounds__(64 * kWaves, MINWG) gqa_rows_kernel(RowParams 
     while (cc < hi) {
         // ---- locate chunk cc: request b, KV head g, chunk k of (b, g) ----
         int lo_b = 0, hi_b = p.B;  // largest b with Hkv * pref[b] <= cc
-        while (hi_b - lo_b > 1) {
-            const int mid = (lo_b + hi_b) >> 1;
-            if ((int64_t)p.Hkv * pref(mid) <= cc) lo_b = mid;
-            else hi_b = mid;
+        if (wave_pref) {  // the prefixes rise with b: count the lanes b < B at or below cc
+            const uint64_t m = __ballot(lane < p.B && (int64_t)p.Hkv * prefv <= cc);
+            lo_b = __popcll(m) - 1;
+        } else {
+            while (hi_b - lo_b > 1) {
+                const int mid = (lo_b + hi_b) >> 1;
+                if ((int64_t)p.Hkv * pref(mid) <= cc) lo_b = mid;
+                else hi_b = mid;
+            }
         }
         const int b = __builtin_amdgcn_readfirstlane(lo_b);
         const int32_t pb = pref(b);

@@ -68,6 +68,21 @@ def test_gqa_bf16_ragged(N, I, bs):
     _check_case(case, range(5), lowp=True)
 
 
+@pytest.mark.parametrize("B", [63, 64, 97])
+def test_gqa_bf16_many_requests(B):
+    """Below 64 requests each wave scans the chunk counts itself and finds a
+    chunk's request by one ballot; from 64 on the kernel takes the
+    workgroup-wide scan and a binary search.  Ragged lengths with empty
+    requests (zero) between long ones, every request checked."""
+    rng = np.random.default_rng(2600 + B)
+    seq = [int(x) for x in rng.integers(0, 3000, size=B)]
+    seq[0], seq[B // 2], seq[-1] = 0, 1, 0
+    w = ci.scaled(ci.WORKLOADS["gqa_decode_bf16"], B=B, seed=2600 + B)
+    announce(f"bf16 B={B} ragged")
+    case = build_decode_case(w, seq=seq, check_cache=False, check_slots=False)
+    _check_case(case, range(B), lowp=True)
+
+
 def test_gqa_bf16_full_workload_sampled():
     w = ci.WORKLOADS["gqa_decode_bf16"]
     announce(f"{w.name} full size, seed={w.seed}")
