@@ -1039,7 +1039,8 @@ def cpu_leg(bench, budget_s: float, one_thread: bool = False) -> dict:
 # The default run adds these to the headline line: the small fp32 case as a
 # latency, and the MLA (bf16, fp8) and prefill workloads with their own roofline
 # (TFLOP/s against the bf16 MFMA peak) and oracle timings.
-EXTRA_WORKLOADS = ["gqa_tiny_f32", "mla_decode_bf16", "mla_decode_fp8", "pcp_prefill_bf16"]
+EXTRA_WORKLOADS = ["gqa_tiny_f32", "mla_decode_bf16", "mla_decode_fp8", "pcp_prefill_bf16",
+                   "dcp_prefill_bf16", "gqa_decode_mtp_bf16", "kv_gather_bf16", "head_scatter_mla"]
 
 
 def extra_block(name: str, steps: int, warmup: int, cpu: bool, budget_s: float) -> dict:
