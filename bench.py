@@ -19,11 +19,21 @@ Other workloads, same step structure:
                     the causal call over the chunk, one call per prefix shard
                     and the merge; the chunk's K/V is first written to the shards
 value = algorithmic FLOP (unmasked score + PV products) / step time (TFLOP/s).
+  dcp_prefill_bf16     the same chunk with its K/V interleaved into the 8 DCP
+                       shards: per PCP rank one causal call per shard + merge
+  gqa_decode_mtp_bf16  the GQA step with 2 query tokens per request
+  kv_gather_bf16       every request's 64K-token window gathered from the 8
+                       shard caches into token order
+  head_scatter_mla     16 layers of the head-scattered output exchange
+                       (correct, pack, packed merge) of an MLA step
+(GB/s for the last three.)
 
 Inputs are synthetic (seeded), resident in HBM before timing starts.  Prints
 ONE JSON line: metric, value, the roofline of the dominant kernel (HIP events
-around each of its launches in the timed region, on the stream it runs on) and
-the fp64 CPU oracle timed on a bounded sample of the same workload.
+around its launches in the timed region, on the stream it runs on), the step
+rate from a HIP-graph replay, and the fp64 CPU oracle timed on a bounded
+sample of the same workload.  The default run adds a `workloads` block with
+the small fp32 latency case and every other workload above.
 """
 from __future__ import annotations
 
