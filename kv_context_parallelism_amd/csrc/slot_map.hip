@@ -102,7 +102,16 @@ __global__ void slot_map_write_kernel(int32_t T, const int32_t *__restrict__ req
     const uint32_t j = idx / per_tok;
     if (j >= (uint32_t)T) return;
     const uint32_t c = idx - j * per_tok;
-    const int64_t s = slot_of(req[j], pos[j], block_table, B, bt_stride, max_blocks, rank, N, I, bs);
+    // the row chunk does not depend on the slot: load it first, so that its
+    // latency overlaps the slot's (position, then block table) loads
+    const int64_t src = (int64_t)j * per_tok + c;
+    const u32x4 kx = k[src];
+    const u32x4 vx = v ? v[src] : u32x4{0u, 0u, 0u, 0u};
+    // request and position in one round trip (not the position after the
+    // request's range check)
+    int32_t rq = req[j], ps = pos[j];
+    asm volatile("" : "+v"(rq), "+v"(ps));
+    const int64_t s = slot_of(rq, ps, block_table, B, bt_stride, max_blocks, rank, N, I, bs);
     if (c == 0 && slot_out) slot_out[j] = s;
     if (s < 0 || s >= num_slots) return;
     const uint32_t h = c / row_chunks;
@@ -116,9 +125,8 @@ __global__ void slot_map_write_kernel(int32_t T, const int32_t *__restrict__ req
         off = s - blk * bs;
     }
     const int64_t dst = ((blk * n_heads + h) * bs + off) * row_chunks + cc;
-    const int64_t src = (int64_t)j * per_tok + c;
-    k_cache[dst] = k[src];
-    if (v) v_cache[dst] = v[src];
+    k_cache[dst] = kx;
+    if (v) v_cache[dst] = vx;
 }
 }  // namespace cpattn
 
