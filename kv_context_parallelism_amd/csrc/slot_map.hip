@@ -65,6 +65,10 @@ __global__ void cache_write_kernel(int32_t T, const int64_t *__restrict__ slot,
     const uint32_t j = idx / per_tok;
     if (j >= (uint32_t)T) return;
     const uint32_t c = idx - j * per_tok;
+    // the row chunk is loaded together with the slot (one round trip)
+    const int64_t src = (int64_t)j * per_tok + c;
+    const u32x4 kx = k[src];
+    const u32x4 vx = v ? v[src] : u32x4{0u, 0u, 0u, 0u};
     const int64_t s = slot[j];
     if (s < 0 || s >= num_slots) return;
     const uint32_t h = c / row_chunks;
@@ -78,9 +82,8 @@ __global__ void cache_write_kernel(int32_t T, const int64_t *__restrict__ slot,
         off = s - blk * bs;
     }
     const int64_t dst = ((blk * n_heads + h) * bs + off) * row_chunks + cc;
-    const int64_t src = (int64_t)j * per_tok + c;
-    k_cache[dst] = k[src];
-    if (v) v_cache[dst] = v[src];
+    k_cache[dst] = kx;
+    if (v) v_cache[dst] = vx;
 }
 
 
