@@ -634,7 +634,9 @@ bool gqa_rows_supported(const cp_gqa_args &a, int T) {
 int gqa_mtp_group_tokens(const cp_gqa_args &a, int T) {
     const int Greal = a.Hkv > 0 ? a.Hq / a.Hkv : 0;
     if (Greal < 1 || Greal > 8 || (Greal & (Greal - 1)) || T < 1) return 0;
-    return T < 8 / Greal ? T : 8 / Greal;
+    int tg = T < 8 / Greal ? T : 8 / Greal;
+    while (tg & (tg - 1)) tg &= tg - 1;  // the kernel takes 1, 2, 4 or 8 rows per KV head
+    return tg;
 }
 
 int gqa_rows_waves(const cp_gqa_args &a, int T, bool mtp) {

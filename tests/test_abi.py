@@ -263,6 +263,15 @@ def test_gqa_mtp_validation():
         assert lib.cp_decode_attn_partial_gqa_mtp(ctypes.byref(m), None, 0, None) == 3, q_len
         sizes[q_len] = lib.cp_workspace_bytes(_lib.CP_OP_DECODE_GQA_MTP, ctypes.byref(m))
     assert 0 < sizes[1] < sizes[2] == sizes[3] == sizes[4] == sizes[7]
+    # groups 2 and 1: q_len 3, 5, 6 and 7 are not powers of two and exceed no
+    # limit; they run as launches of 4, 2 and 1 tokens (at most 8 rows each)
+    for hq, hkv in ((8, 4), (2, 2)):
+        b2 = _lib.CpGqaArgs(**{f: getattr(base, f) for f, _ in base._fields_})
+        b2.Hq, b2.Hkv = hq, hkv
+        for q_len in (3, 5, 6, 7):
+            m = _lib.CpGqaMtpArgs(base=b2, **dict(good, q_len=q_len))
+            assert lib.cp_decode_attn_partial_gqa_mtp(ctypes.byref(m), None, 0, None) == 3, (hq, hkv, q_len)
+            assert lib.cp_workspace_bytes(_lib.CP_OP_DECODE_GQA_MTP, ctypes.byref(m)) > 0
     # groups the row kernel does not take: 16 heads per KV head, or D 64 in bf16
     for over in (dict(Hq=32, Hkv=2), dict(D=64)):
         b2 = _lib.CpGqaArgs(**{f: getattr(base, f) for f, _ in base._fields_})

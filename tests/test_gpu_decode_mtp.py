@@ -84,6 +84,9 @@ def _check(case, q, T, o, l, reqs):
     ("gqa_decode_bf16", 2, 64, 8, [2, 2500, 129]),
     ("gqa_decode_bf16", 5, 16, 8, [5, 1030, 3333]),
     ("gqa_decode_bf16", 11, 8, 8, [11, 700, 4100]),
+    ("gqa_decode_bf16", 3, 16, 8, [3, 1500, 2047]),
+    ("gqa_decode_bf16", 7, 8, 8, [7, 64, 3001]),
+    ("gqa_decode_bf16", 6, 8, 8, [900, 6, 33]),
     ("gqa_tiny_f32", 3, 8, 2, [1000, 3, 260]),
 ])
 def test_mtp_against_oracle(name, T, Hq, Hkv, seq):
