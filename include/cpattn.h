@@ -190,8 +190,8 @@ size_t cp_noalloc_scratch_bytes(void);
  *   base.q   [B][q_len][Hq][D], base.out [B][q_len][Hq][D] fp32,
  *   base.lse [B][q_len][Hq] fp32; other base fields as cp_gqa_args.
  * Supported: 256-byte K/V rows (bf16 D 128 or fp32 D 64), Hq/Hkv in
- * {1, 2, 4, 8}, any q_len >= 1.  The tokens are processed in launches of at
- * most 8 / (Hq/Hkv) tokens (8 query rows per KV head), one after the other on
+ * {1, 2, 4, 8}, any q_len >= 1.  The tokens are processed in launches of a
+ * power of two tokens, at most 8 / (Hq/Hkv) (8 query rows per KV head), one after the other on
  * the stream; each launch reads the shard's K/V once, so q_len * Hq/Hkv above
  * 8 costs ceil(q_len * Hq/Hkv / 8) or more passes over the shard.
  * seq_len[b] < q_len gives NaN rows.
