@@ -133,7 +133,7 @@ struct MlaParams {
     uint32_t q_sign;  // 0x80008000 when the scale is negative (queries negated), else 0
     float v_scale;    // kv_scale (fp8) or 1
     int32_t W;        // tile ranges = workgroups launched
-    float *ws_o;      // [slots][H][512]
+    float *ws_o;      // [slots][H][512] bf16 (the split partials; fp32 LSEs beside them)
     float *ws_l;      // [slots][H]
     int32_t *seg;     // [B][2]
 };
@@ -1014,7 +1014,12 @@ mla_kernel(MlaParams p) {
     if (h2 == 0 && h0 + r32 < p.H)
         p.ws_l[(int64_t)slot * p.H + h0 + r32] =
             bad ? NAN : (empty ? -INFINITY : (m_ref + fast_log2(lt)) * kLn2);
-    float *o_dst = p.ws_o + (int64_t)slot * p.H * kDv + 128 * wave + r32;
+    // bf16 partials, written as whole dwords: lanes 2k and 2k+1 hold columns
+    // 2k and 2k+1 of a head's column block; they swap one value so that the
+    // even lane stores the pair of block cb and the odd lane that of block cb+1.
+    const bool odd = (r32 & 1) != 0;
+    uint32_t *o_dst = reinterpret_cast<uint32_t *>(p.ws_o) +
+                      ((int64_t)slot * p.H * kDv + 128 * wave + (r32 & ~1)) / 2;
 #pragma unroll
     for (int hb = 0; hb < kHb; ++hb)
 #pragma unroll
@@ -1027,10 +1032,14 @@ mla_kernel(MlaParams p) {
                 const int e = 4 * q + r;
                 const int head = 32 * hb + acc_row(e, h2);
                 const float iv = bad ? NAN : (empty ? 0.f : p.v_scale / lv[r]);
-                if (head < p.H) {
 #pragma unroll
-                    for (int cb = 0; cb < kCbW; ++cb)
-                        o_dst[(int64_t)head * kDv + 32 * cb] = o[4 * hb + cb][e] * iv;
+                for (int cb = 0; cb < kCbW; cb += 2) {
+                    const float A = o[4 * hb + cb][e] * iv, B = o[4 * hb + cb + 1][e] * iv;
+                    const float y = __int_as_float(__builtin_amdgcn_mov_dpp(
+                        __float_as_int(odd ? A : B), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+                    if (head < p.H)
+                        o_dst[((int64_t)head * kDv + 32 * (cb + (odd ? 1 : 0))) / 2] =
+                            odd ? pack_bf16x2(y, B) : pack_bf16x2(A, y);
                 }
             }
         }
@@ -1051,7 +1060,7 @@ MlaPlan plan_mla(const cp_mla_args &a) {
     pl.split_tokens = kT;
     pl.nsplit = wgs;  // tile ranges = workgroups launched
     const size_t slots = (size_t)wgs + (size_t)(a.B > 0 ? a.B : 0);
-    pl.ws_bytes = slots * (size_t)a.H * (kDv + 1) * sizeof(float) + (size_t)a.B * 2 * 4 + 512;
+    pl.ws_bytes = slots * (size_t)a.H * (kDv * sizeof(uint16_t) + sizeof(float)) + (size_t)a.B * 2 * 4 + 512;
     return pl;
 }
 
@@ -1096,7 +1105,7 @@ extern "C" cp_status cp_decode_attn_partial_mla(const cp_mla_args *a, void *ws, 
                     pl.ws_bytes, ws_bytes);
     const size_t slots = (size_t)pl.nsplit + (size_t)a->B;
     float *ws_o = static_cast<float *>(ws);
-    float *ws_l = ws_o + slots * a->H * kDv;
+    float *ws_l = ws_o + slots * a->H * kDv / 2;  // after the bf16 partial outputs
     int32_t *seg = reinterpret_cast<int32_t *>(
         (reinterpret_cast<uintptr_t>(ws_l + slots * a->H) + 255) & ~uintptr_t(255));
 
@@ -1145,6 +1154,7 @@ extern "C" cp_status cp_decode_attn_partial_mla(const cp_mla_args *a, void *ws, 
     m.Dv = kDv;
     m.part_out = ws_o;
     m.part_lse = ws_l;
+    m.part_bf16 = true;
     m.o_part_stride = (int64_t)a->H * kDv;
     m.o_row_stride = kDv;
     m.l_part_stride = a->H;

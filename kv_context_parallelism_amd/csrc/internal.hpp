@@ -67,8 +67,9 @@ struct MergeDesc {
     int32_t n_parts;
     int64_t rows;
     int32_t Dv;
-    const float *part_out;
+    const float *part_out;  // fp32 partial outputs, or bf16 when part_bf16 (strides in elements)
     const float *part_lse;
+    bool part_bf16 = false;
     int64_t o_part_stride, o_row_stride;
     int64_t l_part_stride, l_row_stride;
     void *out;

@@ -34,23 +34,40 @@ constexpr int kLaneParts = 64;        // parts per row above which the block ker
 constexpr int kLaneCols = 4;          // float4 columns per lane (Dv <= 64 * 4 * 4)
 
 // Rows of the merge: parts, LSE and output base of row r (plain or segmented).
+// The output base is an element offset into part_out (fp32 or bf16 elements).
 struct RowParts {
-    const float *lp, *op;
+    const float *lp;
+    int64_t oe;
     int32_t n;
 };
 __device__ __forceinline__ RowParts row_parts(const MergeDesc &m, int64_t row) {
     RowParts rp;
     rp.lp = m.part_lse + row * m.l_row_stride;
-    rp.op = m.part_out + row * m.o_row_stride;
+    rp.oe = row * m.o_row_stride;
     rp.n = m.n_parts;
     if (m.seg) {  // parts of this row live at slots first .. first+count-1
         const int64_t grp = row / m.rows_per_seg, sub = row % m.rows_per_seg;
         const int64_t first = m.seg[2 * grp];
         rp.n = m.seg[2 * grp + 1];
         rp.lp = m.part_lse + first * m.l_part_stride + sub * m.l_row_stride;
-        rp.op = m.part_out + first * m.o_part_stride + sub * m.o_row_stride;
+        rp.oe = first * m.o_part_stride + sub * m.o_row_stride;
     }
     return rp;
+}
+
+// Four consecutive partial-output elements from element offset e (a multiple
+// of 4): one 16-byte fp32 load, or one 8-byte load of bf16 values widened
+// exactly.  The element type is a template flag, so that a batch's loads
+// are one straight run of instructions.
+template <bool kBf16In>
+__device__ __forceinline__ float4 load_part4(const MergeDesc &m, int64_t e) {
+    if constexpr (kBf16In) {
+        const u32x2 w = *reinterpret_cast<const u32x2 *>(
+            reinterpret_cast<const uint16_t *>(m.part_out) + e);
+        return make_float4(__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                           __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u));
+    }
+    return *reinterpret_cast<const float4 *>(m.part_out + e);
 }
 
 // Lane-parallel merge: lane j of a kS-lane group owns float4 columns
@@ -59,7 +76,7 @@ __device__ __forceinline__ RowParts row_parts(const MergeDesc &m, int64_t row) {
 // dependent round trip from an LSE to its output), then the running maximum
 // is raised to the batch's and the earlier sums are rescaled by
 // exp(old max - new max) -- a no-op for rows of at most eight parts.
-template <bool kBf16Out, int kS, int kCols>
+template <bool kBf16Out, int kS, int kCols, bool kBf16In>
 __global__ void __launch_bounds__(kThreads) merge_lanes_kernel(MergeDesc m) {
     constexpr int kRowsPerBlock = kThreads / kS;
     constexpr int kBatch = 8;
@@ -82,12 +99,26 @@ __global__ void __launch_bounds__(kThreads) merge_lanes_kernel(MergeDesc m) {
                 L[j] = i0 + j < rp.n ? rp.lp[(int64_t)(i0 + j) * m.l_part_stride] : -INFINITY;
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
-                const float *op = rp.op + (int64_t)(i0 + j) * m.o_part_stride;
+                if constexpr (kBf16In) {
+                    // Unconditional loads from clamped (valid) addresses, then a
+                    // select: a load under a condition would be widened inside
+                    // its branch and wait there, one load at a time.
+                    const int jj = i0 + j < rp.n ? i0 + j : rp.n - 1;
+                    const int64_t oe = rp.oe + (int64_t)jj * m.o_part_stride;
 #pragma unroll
-                for (int cc = 0; cc < kCols; ++cc) {
-                    const int c = lane_g + cc * kS;
-                    o[j][cc] = i0 + j < rp.n && c < n4 ? *reinterpret_cast<const float4 *>(op + 4 * c)
-                                                        : make_float4(0.f, 0.f, 0.f, 0.f);
+                    for (int cc = 0; cc < kCols; ++cc) {
+                        const int c = lane_g + cc * kS;
+                        const float4 v = load_part4<true>(m, oe + 4 * (c < n4 ? c : n4 - 1));
+                        o[j][cc] = i0 + j < rp.n && c < n4 ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+                    }
+                } else {
+                    const int64_t oe = rp.oe + (int64_t)(i0 + j) * m.o_part_stride;
+#pragma unroll
+                    for (int cc = 0; cc < kCols; ++cc) {
+                        const int c = lane_g + cc * kS;
+                        o[j][cc] = i0 + j < rp.n && c < n4 ? load_part4<false>(m, oe + 4 * c)
+                                                            : make_float4(0.f, 0.f, 0.f, 0.f);
+                    }
                 }
             }
             float bmax = lmax;
@@ -96,7 +127,10 @@ __global__ void __launch_bounds__(kThreads) merge_lanes_kernel(MergeDesc m) {
                 nan |= (L[j] != L[j]);
                 bmax = fmaxf(bmax, L[j]);
             }
-            if (bmax == -INFINITY) continue;  // every part so far is empty
+            // every part so far is empty: nothing to add (with bf16 parts the
+            // batch falls through instead, adding zeros, so that its loads are
+            // not moved below this test and issued after the LSEs arrive)
+            if (!kBf16In && bmax == -INFINITY) continue;
             if (bmax != lmax) {               // rescale the earlier sums to the new maximum
                 const float sc = lmax == -INFINITY ? 0.f : expf(lmax - bmax);
                 asum *= sc;
@@ -163,7 +197,7 @@ __device__ __forceinline__ float block_reduce(float v, bool is_max, float *s_red
     return v;
 }
 
-template <bool kBf16Out>
+template <bool kBf16Out, bool kBf16In>
 __global__ void __launch_bounds__(kThreads) merge_rows_kernel(MergeDesc m) {
     __shared__ float s_w[kCachedWeights];
     __shared__ float s_red[kThreads / 64];
@@ -171,7 +205,7 @@ __global__ void __launch_bounds__(kThreads) merge_rows_kernel(MergeDesc m) {
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x;
     const RowParts rp = row_parts(m, row);
-    const float *lp = rp.lp, *obase = rp.op;
+    const float *lp = rp.lp;
     m.n_parts = rp.n;
 
     // 1. l = max_i L_i (NaN anywhere poisons the row)
@@ -206,7 +240,7 @@ __global__ void __launch_bounds__(kThreads) merge_rows_kernel(MergeDesc m) {
         const int c = cb + c0;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
         if (!empty && gi < G && c < n4) {
-            const float *op = obase + 4 * (int64_t)c;
+            const int64_t oc = rp.oe + 4 * (int64_t)c;
             for (int i = gi; i < m.n_parts; i += G) {
                 float a;
                 if (i < kCachedWeights) {
@@ -216,8 +250,7 @@ __global__ void __launch_bounds__(kThreads) merge_rows_kernel(MergeDesc m) {
                     a = (L == -INFINITY) ? 0.f : expf(L - lmax);
                 }
                 if (a > 0.f) {  // an empty part's output is never read
-                    const float4 o =
-                        *reinterpret_cast<const float4 *>(op + (int64_t)i * m.o_part_stride);
+                    const float4 o = load_part4<kBf16In>(m, oc + (int64_t)i * m.o_part_stride);
                     acc.x += a * o.x;
                     acc.y += a * o.y;
                     acc.z += a * o.z;
@@ -270,13 +303,13 @@ int device_cus() {
     return cached[dev];
 }
 
-template <bool kBf16Out, int kS, int kCols>
+template <bool kBf16Out, bool kBf16In, int kS, int kCols>
 void launch_lanes(const MergeDesc &m, hipStream_t stream) {
     constexpr int kRowsPerBlock = kThreads / kS;
     const int64_t need = (m.rows + kRowsPerBlock - 1) / kRowsPerBlock;
     const int64_t cap = (int64_t)device_cus() * 16;  // resident blocks, with margin
     const unsigned grid = (unsigned)(need < cap ? need : cap);
-    hipLaunchKernelGGL((merge_lanes_kernel<kBf16Out, kS, kCols>), dim3(grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((merge_lanes_kernel<kBf16Out, kS, kCols, kBf16In>), dim3(grid), dim3(kThreads), 0,
                        stream, m);
 }
 
@@ -287,22 +320,22 @@ void launch_lanes(const MergeDesc &m, hipStream_t stream) {
 // counts twice).  A split combine (segment table) always takes it: its rows
 // have a few parts each, which one batch of loads covers, and that beats the
 // block kernel's dependent passes even on 1,024 rows (GQA decode combine).
-template <bool kBf16Out>
+template <bool kBf16Out, bool kBf16In>
 bool launch_lanes_for(const MergeDesc &m, hipStream_t stream) {
     const int n4 = m.Dv / 4;
     int S = 1;
     while (S < n4 && S < 64) S *= 2;
     const int cols = (n4 + S - 1) / S;
     if (!m.seg && m.rows * S * cols < (int64_t)device_cus() * 512) return false;
-    if (n4 <= 1) launch_lanes<kBf16Out, 1, 1>(m, stream);
-    else if (n4 <= 2) launch_lanes<kBf16Out, 2, 1>(m, stream);
-    else if (n4 <= 4) launch_lanes<kBf16Out, 4, 1>(m, stream);
-    else if (n4 <= 8) launch_lanes<kBf16Out, 8, 1>(m, stream);
-    else if (n4 <= 16) launch_lanes<kBf16Out, 16, 1>(m, stream);
-    else if (n4 <= 32) launch_lanes<kBf16Out, 32, 1>(m, stream);
-    else if (n4 <= 64) launch_lanes<kBf16Out, 64, 1>(m, stream);
-    else if (n4 <= 128) launch_lanes<kBf16Out, 64, 2>(m, stream);
-    else if (n4 <= 64 * kLaneCols) launch_lanes<kBf16Out, 64, kLaneCols>(m, stream);
+    if (n4 <= 1) launch_lanes<kBf16Out, kBf16In, 1, 1>(m, stream);
+    else if (n4 <= 2) launch_lanes<kBf16Out, kBf16In, 2, 1>(m, stream);
+    else if (n4 <= 4) launch_lanes<kBf16Out, kBf16In, 4, 1>(m, stream);
+    else if (n4 <= 8) launch_lanes<kBf16Out, kBf16In, 8, 1>(m, stream);
+    else if (n4 <= 16) launch_lanes<kBf16Out, kBf16In, 16, 1>(m, stream);
+    else if (n4 <= 32) launch_lanes<kBf16Out, kBf16In, 32, 1>(m, stream);
+    else if (n4 <= 64) launch_lanes<kBf16Out, kBf16In, 64, 1>(m, stream);
+    else if (n4 <= 128) launch_lanes<kBf16Out, kBf16In, 64, 2>(m, stream);
+    else if (n4 <= 64 * kLaneCols) launch_lanes<kBf16Out, kBf16In, 64, kLaneCols>(m, stream);
     else return false;
     return true;
 }
@@ -314,16 +347,20 @@ cp_status launch_merge(const MergeDesc &m, hipStream_t stream) {
     // the lane-parallel kernel (a segment table's counts are a few per row by
     // construction of the decode schedules).
     if (m.seg || m.n_parts <= kLaneParts) {
-        const bool ok = m.out_dt == CP_BF16 ? launch_lanes_for<true>(m, stream)
-                                            : launch_lanes_for<false>(m, stream);
+        const bool ok = m.part_bf16 ? (m.out_dt == CP_BF16 ? launch_lanes_for<true, true>(m, stream)
+                                                           : launch_lanes_for<false, true>(m, stream))
+                                    : (m.out_dt == CP_BF16 ? launch_lanes_for<true, false>(m, stream)
+                                                           : launch_lanes_for<false, false>(m, stream));
         if (ok) return check_launch("lse merge");
     }
-    if (m.out_dt == CP_BF16)
-        hipLaunchKernelGGL(merge_rows_kernel<true>, dim3((unsigned)m.rows), dim3(kThreads), 0,
-                           stream, m);
-    else
-        hipLaunchKernelGGL(merge_rows_kernel<false>, dim3((unsigned)m.rows), dim3(kThreads), 0,
-                           stream, m);
+    const dim3 g((unsigned)m.rows), b(kThreads);
+    if (m.part_bf16) {
+        if (m.out_dt == CP_BF16) hipLaunchKernelGGL((merge_rows_kernel<true, true>), g, b, 0, stream, m);
+        else hipLaunchKernelGGL((merge_rows_kernel<false, true>), g, b, 0, stream, m);
+    } else {
+        if (m.out_dt == CP_BF16) hipLaunchKernelGGL((merge_rows_kernel<true, false>), g, b, 0, stream, m);
+        else hipLaunchKernelGGL((merge_rows_kernel<false, false>), g, b, 0, stream, m);
+    }
     return check_launch("lse merge");
 }
 
