@@ -233,7 +233,10 @@ typedef struct cp_mla_args {
  * 128, B up to 4096 (CP_E_UNSUPPORTED otherwise).
  * Bad lengths / block ids give NaN rows as for GQA.
  * Workspace: cp_workspace_bytes(CP_OP_DECODE_MLA, &args); need not be
- * initialised.
+ * initialised.  The context of a request is split over the GPU's compute
+ * units; the split outputs are held there in bf16 (their LSEs in fp32) and
+ * merged exactly into out/lse, so out carries the rounding of one bf16 store
+ * (relative 2^-9) on top of the kernel's own.
  * Errors: as cp_decode_attn_partial_gqa, plus CP_E_INVALID for num_blocks < 1,
  * a scale that is not finite, or (fp8) a kv_scale that is not positive and
  * finite. */

@@ -53,8 +53,9 @@
 //     blocks of the transposing value reads hit distinct banks;
 //   * a balanced schedule: request b (n_b tiles) is cut into k_b equal tile
 //     ranges with sum k_b <= CUs, one workgroup per range, all resident at
-//     once; partials go to slot = workgroup and are merged exactly afterwards
-//     by a segment table.  Per-request tile counts are prefix-summed per
+//     once; partials go to slot = workgroup (outputs in bf16, half the bytes
+//     of the write here and of the read in the merge; LSEs in fp32) and are
+//     merged exactly afterwards by a segment table.  Per-request tile counts are prefix-summed per
 //     64-request chunk in LDS and resolved within a chunk by a wave scan.
 #include <math.h>
 
