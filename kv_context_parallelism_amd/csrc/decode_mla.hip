@@ -1156,6 +1156,7 @@ extern "C" cp_status cp_decode_attn_partial_mla(const cp_mla_args *a, void *ws, 
     m.part_out = ws_o;
     m.part_lse = ws_l;
     m.part_bf16 = true;
+    m.parts_hint = (int32_t)(pl.nsplit / (a->B > 0 ? a->B : 1));  // tile ranges per request, lengths alike
     m.o_part_stride = (int64_t)a->H * kDv;
     m.o_row_stride = kDv;
     m.l_part_stride = a->H;

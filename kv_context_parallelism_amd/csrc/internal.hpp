@@ -70,6 +70,7 @@ struct MergeDesc {
     const float *part_out;  // fp32 partial outputs, or bf16 when part_bf16 (strides in elements)
     const float *part_lse;
     bool part_bf16 = false;
+    int32_t parts_hint = 0;  // expected parts per row (segment tables): many parts share a row over waves
     int64_t o_part_stride, o_row_stride;
     int64_t l_part_stride, l_row_stride;
     void *out;

@@ -76,14 +76,25 @@ __device__ __forceinline__ float4 load_part4(const MergeDesc &m, int64_t e) {
 // dependent round trip from an LSE to its output), then the running maximum
 // is raised to the batch's and the earlier sums are rescaled by
 // exp(old max - new max) -- a no-op for rows of at most eight parts.
-template <bool kBf16Out, int kS, int kCols, bool kBf16In>
+//
+// kWpr > 1 (rows of many parts): kWpr lane groups of one workgroup share a row,
+// group w taking the batches of parts w*8 .., (w+kWpr)*8 .., each with its
+// own maximum, weight sum and columns; the groups' states are then rescaled
+// to the largest maximum and added through LDS (the same exact rescaling as
+// between batches), so a row's dependent load rounds drop kWpr-fold.
+template <bool kBf16Out, int kS, int kCols, bool kBf16In, int kWpr>
 __global__ void __launch_bounds__(kThreads) merge_lanes_kernel(MergeDesc m) {
-    constexpr int kRowsPerBlock = kThreads / kS;
+    constexpr int kRowsPerBlock = kThreads / kS / kWpr;
     constexpr int kBatch = 8;
+    static_assert(kWpr == 1 || kRowsPerBlock == 1, "groups share a row only one row per block");
     const int lane_g = threadIdx.x % kS;
+    const int sub = kWpr > 1 ? (int)(threadIdx.x / kS) : 0;
     const int n4 = m.Dv / 4;
-    for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / kS; row < m.rows;
-         row += (int64_t)gridDim.x * kRowsPerBlock) {
+    __shared__ float s_m[kWpr], s_s[kWpr];
+    __shared__ int s_nan[kWpr];
+    __shared__ float4 s_acc[kWpr > 1 ? kWpr : 1][kCols][kS];
+    for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (kWpr > 1 ? 0 : threadIdx.x / kS);
+         row < m.rows; row += (int64_t)gridDim.x * kRowsPerBlock) {
         const RowParts rp = row_parts(m, row);
         float lmax = -INFINITY;
         bool nan = false;
@@ -91,7 +102,7 @@ __global__ void __launch_bounds__(kThreads) merge_lanes_kernel(MergeDesc m) {
         float4 acc[kCols];
 #pragma unroll
         for (int cc = 0; cc < kCols; ++cc) acc[cc] = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int i0 = 0; i0 < rp.n; i0 += kBatch) {
+        for (int i0 = sub * kBatch; i0 < rp.n; i0 += kBatch * kWpr) {
             float L[kBatch];
             float4 o[kBatch][kCols];
 #pragma unroll
@@ -158,12 +169,45 @@ __global__ void __launch_bounds__(kThreads) merge_lanes_kernel(MergeDesc m) {
                 }
             }
         }
+        if constexpr (kWpr > 1) {  // add the groups' states in group 0
+            if (lane_g == 0) {
+                s_m[sub] = lmax;
+                s_s[sub] = asum;
+                s_nan[sub] = nan;
+            }
+#pragma unroll
+            for (int cc = 0; cc < kCols; ++cc) s_acc[sub][cc][lane_g] = acc[cc];
+            __syncthreads();
+            if (sub == 0) {
+                float M = -INFINITY;
+                for (int w = 0; w < kWpr; ++w) {
+                    M = fmaxf(M, s_m[w]);
+                    nan |= s_nan[w] != 0;
+                }
+                asum = 0.f;
+#pragma unroll
+                for (int cc = 0; cc < kCols; ++cc) acc[cc] = make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int w = 0; w < kWpr; ++w) {
+                    const float sc = s_m[w] == -INFINITY ? 0.f : expf(s_m[w] - M);
+                    asum += s_s[w] * sc;
+#pragma unroll
+                    for (int cc = 0; cc < kCols; ++cc) {
+                        const float4 v = s_acc[w][cc][lane_g];
+                        acc[cc].x += sc * v.x;
+                        acc[cc].y += sc * v.y;
+                        acc[cc].z += sc * v.z;
+                        acc[cc].w += sc * v.w;
+                    }
+                }
+                lmax = M;
+            }
+        }
         const bool empty = lmax == -INFINITY;
         const float inv = nan ? NAN : (!empty && asum > 0.f ? 1.f / asum : 0.f);
 #pragma unroll
         for (int cc = 0; cc < kCols; ++cc) {
             const int c = lane_g + cc * kS;
-            if (c >= n4) break;
+            if (c >= n4 || sub != 0) break;
             float4 v = empty && !nan ? make_float4(0.f, 0.f, 0.f, 0.f) : acc[cc];
             v.x *= inv;
             v.y *= inv;
@@ -178,8 +222,9 @@ __global__ void __launch_bounds__(kThreads) merge_lanes_kernel(MergeDesc m) {
                 reinterpret_cast<float4 *>(m.out)[merge_out_row(m, row) * n4 + c] = v;
             }
         }
-        if (m.lse_out && lane_g == 0)
+        if (m.lse_out && lane_g == 0 && sub == 0)
             m.lse_out[merge_out_row(m, row)] = nan ? NAN : (empty ? -INFINITY : lmax + logf(asum));
+        if constexpr (kWpr > 1) __syncthreads();  // LDS free for the next row
     }
 }
 
@@ -303,13 +348,13 @@ int device_cus() {
     return cached[dev];
 }
 
-template <bool kBf16Out, bool kBf16In, int kS, int kCols>
+template <bool kBf16Out, bool kBf16In, int kS, int kCols, int kWpr = 1>
 void launch_lanes(const MergeDesc &m, hipStream_t stream) {
-    constexpr int kRowsPerBlock = kThreads / kS;
+    constexpr int kRowsPerBlock = kThreads / kS / kWpr;
     const int64_t need = (m.rows + kRowsPerBlock - 1) / kRowsPerBlock;
     const int64_t cap = (int64_t)device_cus() * 16;  // resident blocks, with margin
     const unsigned grid = (unsigned)(need < cap ? need : cap);
-    hipLaunchKernelGGL((merge_lanes_kernel<kBf16Out, kS, kCols, kBf16In>), dim3(grid), dim3(kThreads), 0,
+    hipLaunchKernelGGL((merge_lanes_kernel<kBf16Out, kS, kCols, kBf16In, kWpr>), dim3(grid), dim3(kThreads), 0,
                        stream, m);
 }
 
@@ -334,6 +379,7 @@ bool launch_lanes_for(const MergeDesc &m, hipStream_t stream) {
     else if (n4 <= 16) launch_lanes<kBf16Out, kBf16In, 16, 1>(m, stream);
     else if (n4 <= 32) launch_lanes<kBf16Out, kBf16In, 32, 1>(m, stream);
     else if (n4 <= 64) launch_lanes<kBf16Out, kBf16In, 64, 1>(m, stream);
+    else if (n4 <= 128 && m.parts_hint >= 16) launch_lanes<kBf16Out, kBf16In, 64, 2, 4>(m, stream);
     else if (n4 <= 128) launch_lanes<kBf16Out, kBf16In, 64, 2>(m, stream);
     else if (n4 <= 64 * kLaneCols) launch_lanes<kBf16Out, kBf16In, 64, kLaneCols>(m, stream);
     else return false;
